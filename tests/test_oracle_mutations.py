@@ -1,0 +1,79 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each one.
+import os, sys; sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+Each mutation patches one oracle function for the duration of the test. A
+pin that still passes under the mutation would be a pin that cannot see that
+mistake.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import paging as P
+import test_oracle_attention as TA
+import test_oracle_paging as TP
+import test_oracle_cache_write as TW
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    orig = A.softmax_attend
+    monkeypatch.setattr(A, "softmax_attend", lambda q, K, V, scale: orig(q, K, V, 1.0))
+    _fails(TA.test_decode_matches_bruteforce_contiguous, "f16", 8, 8)
+
+
+def test_wrong_head_grouping_is_caught(monkeypatch):
+    # Interleaved grouping (h % Hkv) instead of consecutive (h // g).
+    def bad(q_bits, dtype, ki, kv, vi, vv, layer, bt, ctx, bs, Hkv, D, scale, select=None):
+        q = q_bits.copy()
+        Hq = q.shape[1]
+        perm = [(h % Hkv) * (Hq // Hkv) + h // Hkv for h in range(Hq)]
+        out = orig(q[:, perm], dtype, ki, kv, vi, vv, layer, bt, ctx, bs, Hkv, D, scale, select)
+        res = np.empty_like(out)
+        res[:, perm] = out
+        return res
+    orig = A.paged_decode
+    monkeypatch.setattr(A, "paged_decode", bad)
+    _fails(TA.test_head_grouping_matches_page)
+
+
+def test_causal_off_by_one_is_caught(monkeypatch):
+    orig = A.softmax_attend
+    monkeypatch.setattr(A, "softmax_attend",
+                        lambda q, K, V, s: orig(q, K[:-1], V[:-1], s) if len(K) > 1 else orig(q, K, V, s))
+    _fails(TA.test_chunk_rows_match_decode_causal_and_unchunked)
+
+
+def test_transposed_slot_split_is_caught(monkeypatch):
+    monkeypatch.setattr(P, "split_slot", lambda slot, bs: (int(slot) % int(bs), int(slot) // int(bs)))
+    _fails(TP.test_slot_322_from_page)
+
+
+def test_wrong_mla_scale_group_is_caught(monkeypatch):
+    def bad(rows):
+        lat, rope = orig(rows)
+        return lat[:, ::-1].copy(), rope          # latent values paired with the wrong positions
+    orig = A.mla_parse_rows
+    monkeypatch.setattr(A, "mla_parse_rows", bad)
+    _fails(TA.test_mla_matches_bruteforce_with_library_fp8_decode)
+
+
+def test_wrong_layer_stride_is_caught(monkeypatch):
+    monkeypatch.setattr(P, "address", lambda v, layer, b, pos: v.offset + b * v.block_stride + pos * v.row_bytes)
+    _fails(TP.test_blhnc_pages_views_and_addresses_from_page)
+
+
+def test_missing_max_subtraction_in_merge_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "merge_partitions", lambda ms, ls, accs: (accs.sum(0)) / ls.sum())
+    _fails(TA.test_partition_merge_identity, 16)
+
+
+def test_write_at_wrong_row_is_caught(monkeypatch):
+    orig = P.address
+    monkeypatch.setattr(P, "address", lambda v, layer, b, pos: orig(v, layer, b, (pos + 1) % 16))
+    _fails(TW.test_round_trip_and_untouched_bytes)

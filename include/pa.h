@@ -1,0 +1,214 @@
+/*
+ * pa.h: C ABI of the paged-KV-cache hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes two things. First, attention over a KV cache stored in
+ * fixed-size, non-contiguous physical blocks, addressed through a per-request
+ * block table. Second, the reshape_and_cache write that scatters new K/V rows
+ * into those blocks through slot_mapping.
+ *
+ * Sources, cited by page title and section:
+ *   [MEM]    "deep dive into vLLM 05: KV cache memory core" (arganzheng.life)
+ *   [LAYOUT] "vLLM KV Cache Layout 可视化" (riverclouds.net)
+ *   [MGMT]   "KV Cache 与推理服务内存管理" (pinghaoyang.com.cn)
+ *   [INSIDE] "vLLM 技术内幕——像操作系统管理内存一样管理 KV 缓存" (openeuler.csdn.net)
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: every pointer argument is caller-owned memory. "Device" means
+ *     memory the GPU can read (hipMalloc / torch CUDA tensors); descriptors are
+ *     host memory. The library allocates nothing, keeps no state between calls
+ *     and may be called from several host threads.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *     stream). Work is enqueued asynchronously; no call synchronises or reads
+ *     device memory on the host.
+ *   - Errors: arguments the host can check (null pointers, sizes, formats,
+ *     alignment, view extents against the stated allocation size, workspace
+ *     size) are validated before anything is enqueued. A failed check returns
+ *     a non-zero pa_status and enqueues nothing. A failed launch returns
+ *     PA_ERR_HIP; pa_last_hip_error() gives the HIP error code.
+ *   - Device-side values (slots, block ids, context lengths) cannot be checked
+ *     on the host. The kernels bound them instead, so that a bad value never
+ *     leads to an access outside the cache:
+ *       * a slot outside [0, num_blocks*block_size) is skipped;
+ *       * a block-table entry outside [0, num_blocks) contributes no tokens;
+ *       * a context length is clamped to
+ *         [0, min(max_context_len, bt_stride*block_size)].
+ *     Results for such inputs are unspecified but memory-safe.
+ *   - Byte order is little-endian throughout.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL_POINTER = 1,      /* a required pointer is NULL */
+    PA_ERR_INVALID_ARGUMENT = 2,  /* negative count, inconsistent sizes, reserved field not 0 */
+    PA_ERR_UNSUPPORTED = 3,       /* format, head size, head ratio or block size not implemented */
+    PA_ERR_MISALIGNED = 4,        /* a pointer, stride or row width breaks the stated alignment */
+    PA_ERR_VIEW_OUT_OF_RANGE = 5, /* a cache view's rows reach past the stated allocation size */
+    PA_ERR_WORKSPACE = 6,         /* workspace NULL or smaller than the *_workspace_bytes query */
+    PA_ERR_HIP = 7                /* a HIP launch failed; see pa_last_hip_error() */
+} pa_status;
+
+/* KV storage formats.
+ *   PA_KV_F16, PA_KV_BF16: dense rows. One token's row holds num_kv_heads
+ *     heads of head_dim 16-bit values, head-major ([num_kv_heads, head_dim]),
+ *     so a per-layer cache has the [num_blocks, block_size, num_kv_heads,
+ *     head_dim] shape given in [MEM] §1.2. Queries and outputs use the same
+ *     16-bit type.
+ *   PA_KV_MLA656_E4M3: the 656-byte MLA row of [LAYOUT] (section on two caches
+ *     sharing one block table). Bytes [0,512) hold 512 OCP e4m3 latent values.
+ *     Bytes [512,528) hold 4 float32 scales; scale k multiplies latent values
+ *     [128k, 128k+128). Bytes [528,656) hold 64 bf16 RoPE values. Queries are
+ *     bf16 [.., num_q_heads, 576] (512 latent dims, then 64 RoPE dims).
+ *     Outputs are bf16 [.., num_q_heads, 512]: the softmax-weighted
+ *     dequantized latent ([MEM] §3.3: attention stays in latent space).
+ */
+typedef enum pa_kv_format {
+    PA_KV_F16 = 0,
+    PA_KV_BF16 = 1,
+    PA_KV_MLA656_E4M3 = 2
+} pa_kv_format;
+
+/* One view over a flat cache allocation: the KVCacheTensor parameters of
+ * [LAYOUT] (section "block ID 只是个编号") plus the row width. The row of
+ * (layer, block b, position pos) starts at
+ *     base + offset + layer*layer_stride + b*block_stride + pos*row_bytes.
+ * Layer-outer layouts have block_stride = page and
+ * layer_stride = page*num_blocks. Block-outer layouts have
+ * layer_stride = page and block_stride = the bytes of a whole block
+ * ([LAYOUT], layout section). All fields are byte counts >= 0. */
+typedef struct pa_cache_view {
+    int64_t offset;
+    int64_t layer_stride;
+    int64_t block_stride;
+    int32_t row_bytes;
+    int32_t reserved;             /* must be 0 */
+} pa_cache_view;
+
+/* Static description of an attention call's cache and heads (host memory). */
+typedef struct pa_attn_desc {
+    int32_t kv_format;            /* pa_kv_format */
+    int32_t num_q_heads;          /* query heads */
+    int32_t num_kv_heads;         /* K/V heads; num_q_heads % num_kv_heads == 0. Query head h reads
+                                     K/V head h / (num_q_heads/num_kv_heads) ([MEM] §3.2). MLA: 1 */
+    int32_t qk_dim;               /* dense: head_dim (64, 128 or 256). MLA: 576 */
+    int32_t v_dim;                /* dense: == qk_dim. MLA: 512 */
+    int32_t block_size;           /* tokens per block: a multiple of 16, at most 256 */
+    int32_t layer;                /* layer index applied to the views' layer_stride */
+    int32_t partition_size;       /* decode only: tokens per split-context partition; 0 lets the
+                                     library choose; otherwise a positive multiple of block_size */
+    int64_t num_blocks;           /* physical blocks addressable through the views */
+    pa_cache_view k_view;         /* K rows (MLA: the 656-byte rows) */
+    pa_cache_view v_view;         /* V rows (dense only; ignored for MLA) */
+    int64_t k_cache_bytes;        /* size of the allocation at k_cache, for the extent check */
+    int64_t v_cache_bytes;        /* size of the allocation at v_cache (dense only) */
+} pa_attn_desc;
+
+/* ABI version of the loaded library (PA_ABI_VERSION). */
+int32_t pa_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* pa_status_string(int32_t status);
+
+/* HIP error code (hipError_t) of the last PA_ERR_HIP on the calling host thread, else 0. */
+int32_t pa_last_hip_error(void);
+
+/* reshape_and_cache: scatter new rows into one or two cache views through one slot_mapping.
+ *
+ * Defined by [LAYOUT], section "kernel 那一侧": each token's slot is split into
+ * block = slot / block_size and position = slot % block_size. The row is
+ * written at base + offset + layer*layer_stride + block*block_stride +
+ * position*row_bytes, using that view's own strides. [INSIDE] §2.1 names the
+ * fused operator; [MGMT] shows a decode step writing the new token's K/V at
+ * (physical block, offset in block).
+ *
+ *   k, v           device; row t of each source starts at k + t*k_pitch (v + t*v_pitch) and holds
+ *                  k_view.row_bytes (v_view.row_bytes) bytes, copied bit-exactly. v may be NULL to
+ *                  write only the k view. For dense caches the source rows are [num_kv_heads,
+ *                  head_dim] values. For the DSA dual cache of [LAYOUT], k carries packed MLA rows
+ *                  and v packed indexer rows.
+ *   slot_mapping   device int64 [num_tokens]: physical block*block_size + in-block position. A
+ *                  negative slot marks padding and is skipped. Two tokens with the same slot in one
+ *                  call race (caller error).
+ *   k_cache, v_cache  device allocation bases; *_cache_bytes give their sizes.
+ *   layer          layer index into the views' layer_stride.
+ *   block_size, num_blocks  the pool geometry (slot < num_blocks*block_size).
+ * Alignment: every address involved must be 4-byte aligned (row_bytes, pitches, strides, offsets,
+ * bases). 16-byte alignment of all of them selects the 16-byte copy path.
+ * num_tokens == 0 is a no-op. */
+int32_t pa_reshape_and_cache(const void* k, int64_t k_pitch, const void* v, int64_t v_pitch,
+                             const int64_t* slot_mapping, int32_t num_tokens,
+                             void* k_cache, int64_t k_cache_bytes, pa_cache_view k_view,
+                             void* v_cache, int64_t v_cache_bytes, pa_cache_view v_view,
+                             int32_t layer, int32_t block_size, int64_t num_blocks, void* stream);
+
+/* Workspace bytes pa_decode needs for this shape (0 when no split-context partials are needed). */
+size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t max_context_len);
+
+/* pa_decode: one query token per sequence attends to its whole paged context.
+ *
+ * out[b, h] = softmax_t(scale * q[b, h] . K_t) applied to V_t, for tokens t in [0, context_lens[b]).
+ * Token t of sequence b is read from physical block block_tables[b*bt_stride + t/block_size] at
+ * position t % block_size ([MEM] §2 read path; [MGMT] paged_attention; [INSIDE] §2.1: the kernel
+ * knows only the block table and reads block by block). The softmax runs online over blocks and over
+ * split-context partitions merged by log-sum-exp; both are exact rearrangements, computed in fp32.
+ *
+ *   out            device [num_seqs, num_q_heads, v_dim] in the query type (dense: the KV type;
+ *                  MLA: bf16). Rounded to nearest even.
+ *   q              device [num_seqs, num_q_heads, qk_dim], contiguous.
+ *   k_cache, v_cache  device allocation bases of the K and V views (v_cache unused and may be NULL
+ *                  for MLA).
+ *   block_tables   device int32 [num_seqs, bt_stride]; entries past ceil(ctx/block_size) are not read.
+ *   context_lens   device int32 [num_seqs]: tokens to attend, the current one included (the caller
+ *                  writes it first). 0 gives an output of 0.
+ *   max_context_len  host upper bound of context_lens; sizes the grid.
+ *   scale          softmax scale (e.g. 1/sqrt(qk_dim)).
+ *   workspace      device scratch of at least pa_decode_workspace_bytes(...) bytes (may be NULL when
+ *                  that is 0). Its contents on entry do not matter.
+ * Alignment: q, out, cache bases, view offsets, strides and row_bytes: 16 bytes.
+ * num_seqs == 0 is a no-op. */
+int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                  int32_t num_seqs, int32_t max_context_len, float scale, const pa_attn_desc* desc,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_prefill_chunk needs. */
+size_t pa_prefill_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t total_q,
+                                  int32_t max_query_len, int32_t max_seq_len);
+
+/* pa_prefill_chunk: causal query chunks attending to already-cached paged context (varlen).
+ *
+ * [INSIDE] §3.2: a long prompt is processed in chunks under a per-step token budget. Each chunk
+ * attends causally to the context already in the cache, and decodes run in the same step. Sequence
+ * b owns query rows [query_start_loc[b], query_start_loc[b+1]). Its seq_lens[b] tokens, this chunk's
+ * included, are in the cache (written first, as for decode). Query row i of sequence b sits at
+ * absolute position a = seq_lens[b] - qlen_b + i and attends to tokens [0, a]. A decode is a chunk of
+ * length 1.
+ *
+ *   out            device [total_q, num_q_heads, v_dim] in the query type.
+ *   q              device [total_q, num_q_heads, qk_dim].
+ *   seq_lens       device int32 [num_seqs]; query_start_loc device int32 [num_seqs+1], with
+ *                  query_start_loc[0] == 0 and query_start_loc[num_seqs] == total_q; qlen_b <= seq_lens[b].
+ *   max_query_len, max_seq_len  host upper bounds of qlen_b and seq_lens[b]; size the grid.
+ *   Other arguments as for pa_decode. Dense formats only. */
+int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q,
+                         int32_t max_query_len, int32_t max_seq_len, float scale,
+                         const pa_attn_desc* desc, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

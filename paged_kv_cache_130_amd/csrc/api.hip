@@ -1,0 +1,238 @@
+// Host side of the C ABI in include/pa.h: argument validation, kernel selection, launch.
+// Every check runs before anything is enqueued; no call reads device memory on the host.
+
+#include <cmath>
+#include <cstring>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+int32_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return PA_OK;
+    g_last_hip_error = (int32_t)e;
+    return PA_ERR_HIP;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+bool aligned(int64_t v, int64_t a) { return (v & (a - 1)) == 0; }
+
+// A view is well formed when its fields are non-negative, its rows are non-empty, one block's rows
+// fit in a block stride (so blocks do not overlap), and every row of `layer` for blocks
+// [0, num_blocks) lies inside [0, cache_bytes).
+int32_t check_view(const pa_cache_view& v, int32_t layer, int64_t num_blocks, int32_t block_size,
+                   int64_t cache_bytes) {
+    if (v.reserved != 0 || v.offset < 0 || v.layer_stride < 0 || v.block_stride < 0 || v.row_bytes <= 0)
+        return PA_ERR_INVALID_ARGUMENT;
+    if (layer < 0 || num_blocks <= 0 || block_size <= 0 || cache_bytes <= 0) return PA_ERR_INVALID_ARGUMENT;
+    const __int128 page = (__int128)block_size * v.row_bytes;
+    if (num_blocks > 1 && page > v.block_stride) return PA_ERR_INVALID_ARGUMENT;
+    const __int128 end = (__int128)v.offset + (__int128)layer * v.layer_stride +
+                         (__int128)(num_blocks - 1) * v.block_stride + page;
+    if (end > cache_bytes) return PA_ERR_VIEW_OUT_OF_RANGE;
+    return PA_OK;
+}
+
+bool view_aligned(const pa_cache_view& v, int32_t layer, int64_t a) {
+    return aligned(v.offset, a) && aligned((int64_t)layer * v.layer_stride, a) && aligned(v.block_stride, a) &&
+           aligned((int64_t)v.row_bytes, a);
+}
+
+constexpr int32_t kMaxBlockSize = 256;
+constexpr int32_t kDefaultPartition = 512;
+
+bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= kMaxBlockSize && bs % 16 == 0; }
+
+// Tokens per split-context partition. A requested size is a multiple of block_size; partitions are
+// capped at 64 blocks, because a partition's block ids are held one per lane of a wave.
+int32_t effective_partition(const pa_attn_desc& d) {
+    int32_t P = d.partition_size > 0 ? d.partition_size : kDefaultPartition;
+    if (P < d.block_size) P = d.block_size;
+    P -= P % d.block_size;
+    const int32_t cap = 64 * d.block_size;
+    return P > cap ? cap : P;
+}
+
+int32_t check_dense_desc(const pa_attn_desc& d) {
+    if (d.kv_format != PA_KV_F16 && d.kv_format != PA_KV_BF16) return PA_ERR_UNSUPPORTED;
+    if (d.num_q_heads <= 0 || d.num_kv_heads <= 0 || d.num_q_heads % d.num_kv_heads != 0)
+        return PA_ERR_INVALID_ARGUMENT;
+    if (d.qk_dim != d.v_dim) return PA_ERR_INVALID_ARGUMENT;
+    if (d.qk_dim != 64 && d.qk_dim != 128 && d.qk_dim != 256) return PA_ERR_UNSUPPORTED;
+    const int32_t g = d.num_q_heads / d.num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8) return PA_ERR_UNSUPPORTED;
+    if (!block_size_ok(d.block_size)) return PA_ERR_UNSUPPORTED;
+    if (d.partition_size < 0 || (d.partition_size > 0 && d.partition_size % d.block_size != 0))
+        return PA_ERR_INVALID_ARGUMENT;
+    const int64_t row = (int64_t)d.num_kv_heads * d.qk_dim * 2;
+    if (d.k_view.row_bytes != row || d.v_view.row_bytes != row) return PA_ERR_INVALID_ARGUMENT;
+    int32_t st = check_view(d.k_view, d.layer, d.num_blocks, d.block_size, d.k_cache_bytes);
+    if (st != PA_OK) return st;
+    st = check_view(d.v_view, d.layer, d.num_blocks, d.block_size, d.v_cache_bytes);
+    if (st != PA_OK) return st;
+    if (!view_aligned(d.k_view, d.layer, 16) || !view_aligned(d.v_view, d.layer, 16)) return PA_ERR_MISALIGNED;
+    if (d.num_blocks > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;  // block ids are int32
+    return PA_OK;
+}
+
+size_t dense_decode_ws(const pa_attn_desc& d, int32_t num_seqs, int32_t max_context_len) {
+    const int32_t P = effective_partition(d);
+    const int64_t parts = ((int64_t)max_context_len + P - 1) / P;
+    if (parts <= 1 || num_seqs <= 0) return 0;
+    const int64_t n = (int64_t)num_seqs * d.num_q_heads * parts;
+    return (size_t)(n * 2 + n * d.v_dim) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(int32_t s) {
+    switch (s) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL_POINTER: return "null pointer";
+        case PA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case PA_ERR_UNSUPPORTED: return "unsupported format or shape";
+        case PA_ERR_MISALIGNED: return "misaligned pointer, stride or row width";
+        case PA_ERR_VIEW_OUT_OF_RANGE: return "cache view reaches past the allocation";
+        case PA_ERR_WORKSPACE: return "workspace missing or too small";
+        case PA_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int32_t pa_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t pa_reshape_and_cache(const void* k, int64_t k_pitch, const void* v, int64_t v_pitch,
+                             const int64_t* slot_mapping, int32_t num_tokens, void* k_cache, int64_t k_cache_bytes,
+                             pa_cache_view k_view, void* v_cache, int64_t v_cache_bytes, pa_cache_view v_view,
+                             int32_t layer, int32_t block_size, int64_t num_blocks, void* stream) {
+    if (num_tokens < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !slot_mapping || !k_cache) return PA_ERR_NULL_POINTER;
+    if (v && !v_cache) return PA_ERR_NULL_POINTER;
+    if (block_size <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_blocks > INT64_MAX / block_size) return PA_ERR_INVALID_ARGUMENT;
+    const int nviews = v ? 2 : 1;
+    const void* src[2] = {k, v};
+    const int64_t pitch[2] = {k_pitch, v_pitch};
+    void* base[2] = {k_cache, v_cache};
+    const int64_t bytes[2] = {k_cache_bytes, v_cache_bytes};
+    const pa_cache_view* view[2] = {&k_view, &v_view};
+    pa::CacheWriteParams p;
+    std::memset(&p, 0, sizeof(p));
+    for (int i = 0; i < nviews; ++i) {
+        int32_t st = check_view(*view[i], layer, num_blocks, block_size, bytes[i]);
+        if (st != PA_OK) return st;
+        if (pitch[i] < view[i]->row_bytes) return PA_ERR_INVALID_ARGUMENT;
+        const bool a4 = aligned(src[i], 4) && aligned(base[i], 4) && aligned(pitch[i], 4) &&
+                        view_aligned(*view[i], layer, 4);
+        if (!a4) return PA_ERR_MISALIGNED;
+        const bool a16 = aligned(src[i], 16) && aligned(base[i], 16) && aligned(pitch[i], 16) &&
+                         view_aligned(*view[i], layer, 16);
+        p.src[i] = static_cast<const char*>(src[i]);
+        p.pitch[i] = pitch[i];
+        p.dst[i] = static_cast<char*>(base[i]) + view[i]->offset + (int64_t)layer * view[i]->layer_stride;
+        p.block_stride[i] = view[i]->block_stride;
+        p.row_bytes[i] = view[i]->row_bytes;
+        p.vec16[i] = a16 ? 1 : 0;
+    }
+    p.slots = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_views = nviews;
+    p.block_size = block_size;
+    p.num_slots = num_blocks * block_size;
+    return hip_status(pa::launch_cache_write(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t max_context_len) {
+    if (!desc || num_seqs <= 0 || max_context_len <= 0) return 0;
+    if (desc->kv_format == PA_KV_F16 || desc->kv_format == PA_KV_BF16) {
+        if (!block_size_ok(desc->block_size)) return 0;
+        return dense_decode_ws(*desc, num_seqs, max_context_len);
+    }
+    return 0;
+}
+
+int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                  int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                  float scale, const pa_attn_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!desc) return PA_ERR_NULL_POINTER;
+    if (num_seqs < 0 || max_context_len < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !q || !k_cache || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
+    if (bt_stride <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+    const pa_attn_desc& d = *desc;
+    if (d.kv_format == PA_KV_MLA656_E4M3) return PA_ERR_UNSUPPORTED;
+    int32_t st = check_dense_desc(d);
+    if (st != PA_OK) return st;
+    if (!v_cache) return PA_ERR_NULL_POINTER;
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return PA_ERR_MISALIGNED;
+    const int32_t P = effective_partition(d);
+    const int64_t max_parts64 = ((int64_t)max_context_len + P - 1) / P;
+    const int32_t max_parts = max_parts64 < 1 ? 1 : (int32_t)max_parts64;
+    const size_t need = dense_decode_ws(d, num_seqs, max_context_len);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return PA_ERR_MISALIGNED;
+    if ((int64_t)d.num_kv_heads * num_seqs * max_parts > 0x7FFFFFFFLL - 64) return PA_ERR_UNSUPPORTED;
+
+    pa::DenseDecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.out = out;
+    p.q = q;
+    p.k = static_cast<const char*>(k_cache) + d.k_view.offset + (int64_t)d.layer * d.k_view.layer_stride;
+    p.v = static_cast<const char*>(v_cache) + d.v_view.offset + (int64_t)d.layer * d.v_view.layer_stride;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    const int64_t n = (int64_t)num_seqs * d.num_q_heads * max_parts;
+    p.part_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
+    p.part_acc = need > 0 ? static_cast<float*>(workspace) + 2 * n : nullptr;
+    p.k_block_stride = d.k_view.block_stride;
+    p.v_block_stride = d.v_view.block_stride;
+    p.num_blocks = d.num_blocks;
+    p.k_row_bytes = d.k_view.row_bytes;
+    p.v_row_bytes = d.v_view.row_bytes;
+    p.bt_stride = bt_stride;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = d.num_q_heads;
+    p.num_kv_heads = d.num_kv_heads;
+    p.block_size = d.block_size;
+    p.partition_tokens = P;
+    p.max_parts = max_parts;
+    p.max_context_len = max_context_len;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.is_bf16 = d.kv_format == PA_KV_BF16;
+    p.head_dim = d.qk_dim;
+    p.group = d.num_q_heads / d.num_kv_heads;
+    return hip_status(pa::launch_decode_dense(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_prefill_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t total_q,
+                                  int32_t max_query_len, int32_t max_seq_len) {
+    (void)desc;
+    (void)num_seqs;
+    (void)total_q;
+    (void)max_query_len;
+    (void)max_seq_len;
+    return 0;
+}
+
+int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q, int32_t max_query_len,
+                         int32_t max_seq_len, float scale, const pa_attn_desc* desc, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    (void)out; (void)q; (void)k_cache; (void)v_cache; (void)block_tables; (void)bt_stride; (void)seq_lens;
+    (void)query_start_loc; (void)num_seqs; (void)total_q; (void)max_query_len; (void)max_seq_len; (void)scale;
+    (void)desc; (void)workspace; (void)workspace_bytes; (void)stream;
+    return PA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Internal launch parameters shared by the host API (api.hip) and the kernel files.
+// Not part of the public ABI; include/pa.h is.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace pa {
+
+// ---------------------------------------------------------------------------
+// reshape_and_cache
+// ---------------------------------------------------------------------------
+struct CacheWriteParams {
+    const char* src[2];        // source rows of view 0 (k) and view 1 (v)
+    int64_t pitch[2];          // bytes between source rows
+    char* dst[2];              // cache base + view offset + layer * layer_stride
+    int64_t block_stride[2];
+    int32_t row_bytes[2];
+    int32_t vec16[2];          // 1: every address of the view is 16-byte aligned
+    const int64_t* slots;      // [num_tokens]
+    int32_t num_tokens;
+    int32_t num_views;         // 1 or 2
+    int32_t block_size;
+    int32_t pad_;
+    int64_t num_slots;         // num_blocks * block_size
+};
+hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Dense paged decode (fp16 / bf16 rows, head_dim 64 / 128 / 256, group <= 8)
+// ---------------------------------------------------------------------------
+struct DenseDecodeParams {
+    void* out;                 // [num_seqs, Hq, D]
+    const void* q;             // [num_seqs, Hq, D]
+    const char* k;             // cache base + view offset + layer * layer_stride
+    const char* v;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* part_ml;            // [num_seqs, Hq, max_parts, 2]: running max (log2 domain), sum
+    float* part_acc;           // [num_seqs, Hq, max_parts, D]: unnormalised accumulator
+    int64_t k_block_stride, v_block_stride;
+    int64_t num_blocks;
+    int32_t k_row_bytes, v_row_bytes;
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t num_q_heads, num_kv_heads;
+    int32_t block_size;
+    int32_t partition_tokens;  // multiple of block_size, <= 64 * block_size
+    int32_t max_parts;         // ceil(max_context_len / partition_tokens)
+    int32_t max_context_len;   // clamp for context_lens
+    float scale_log2;          // softmax scale * log2(e)
+    int32_t is_bf16;
+    int32_t head_dim;
+    int32_t group;             // Hq / Hkv
+};
+hipError_t launch_decode_dense(const DenseDecodeParams& p, hipStream_t stream);
+
+}  // namespace pa

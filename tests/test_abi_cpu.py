@@ -1,0 +1,114 @@
+"""The C ABI without a GPU: the library loads, exports what include/pa.h declares, and rejects bad
+arguments with the documented status before anything is enqueued (no call here reaches a launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_130_amd as pa
+from paged_kv_cache_130_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000           # 64 KiB-aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\*?\s+\*?(pa_[a-z0-9_]+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) >= {"pa_reshape_and_cache", "pa_decode", "pa_prefill_chunk"}
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+    assert pa.abi_version() == 1
+
+
+def test_status_strings():
+    for code in range(8):
+        assert pa.status_string(code) and pa.status_string(code) != "unknown status"
+    assert pa.status_string(99) == "unknown status"
+
+
+def good_desc(**kw):
+    d = pa.dense_desc("f16", 8, 8, 128, 16, 64, 64 * 16 * 2048, 64 * 16 * 2048)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def decode(desc, out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, bt_stride=32, ctx=FAKE, num_seqs=4, max_ctx=300,
+           scale=0.1, ws=None, ws_bytes=0):
+    d = desc.c() if desc is not None else None
+    return L._lib.pa_decode(out, q, k, v, bt, bt_stride, ctx, num_seqs, max_ctx, scale,
+                            ctypes.byref(d) if d is not None else None, ws, ws_bytes, None)
+
+
+def test_decode_status_codes():
+    E = L
+    assert decode(None) == E.PA_ERR_NULL_POINTER
+    assert decode(good_desc(), num_seqs=-1) == E.PA_ERR_INVALID_ARGUMENT
+    assert decode(good_desc(), num_seqs=0) == E.PA_OK                       # no-op, nothing enqueued
+    assert decode(good_desc(), q=None) == E.PA_ERR_NULL_POINTER
+    assert decode(good_desc(), bt_stride=0) == E.PA_ERR_INVALID_ARGUMENT
+    assert decode(good_desc(), scale=float("nan")) == E.PA_ERR_INVALID_ARGUMENT
+    assert decode(good_desc(num_kv_heads=3)) == E.PA_ERR_INVALID_ARGUMENT   # 8 % 3 != 0
+    assert decode(good_desc(num_q_heads=40, num_kv_heads=8)) == E.PA_ERR_UNSUPPORTED  # group 5
+    assert decode(good_desc(qk_dim=96, v_dim=96)) == E.PA_ERR_UNSUPPORTED
+    assert decode(good_desc(v_dim=64)) == E.PA_ERR_INVALID_ARGUMENT
+    assert decode(good_desc(block_size=8)) == E.PA_ERR_UNSUPPORTED
+    assert decode(good_desc(block_size=24)) == E.PA_ERR_UNSUPPORTED
+    assert decode(good_desc(partition_size=40)) == E.PA_ERR_INVALID_ARGUMENT  # not a multiple of 16
+    assert decode(good_desc(kv_format=7)) == E.PA_ERR_UNSUPPORTED
+    bad_row = good_desc()
+    bad_row.k_view = pa.CacheView(0, 0, 16 * 2048, 1024)
+    assert decode(bad_row) == E.PA_ERR_INVALID_ARGUMENT                     # row width != Hkv*D*2
+    small = good_desc(k_cache_bytes=64 * 16 * 2048 - 1)
+    assert decode(small) == E.PA_ERR_VIEW_OUT_OF_RANGE
+    layered = good_desc(layer=1)
+    layered.k_view = pa.CacheView(0, 64 * 16 * 2048, 16 * 2048, 2048)
+    assert decode(layered) == E.PA_ERR_VIEW_OUT_OF_RANGE                    # layer 1 needs 2x the bytes
+    mis = good_desc()
+    mis.k_view = pa.CacheView(8, 0, 16 * 2048, 2048)
+    mis.k_cache_bytes += 8
+    assert decode(mis) == E.PA_ERR_MISALIGNED
+    assert decode(good_desc(), q=FAKE + 4) == E.PA_ERR_MISALIGNED
+    # 4 partitions of 512 are needed for 2048 tokens: the workspace must be given.
+    need = pa.pa_decode_workspace_bytes(good_desc(), 4, 2048)
+    assert need == 4 * 8 * 4 * (2 + 128) * 4
+    assert pa.pa_decode_workspace_bytes(good_desc(), 4, 512) == 0
+    assert decode(good_desc(), max_ctx=2048) == E.PA_ERR_WORKSPACE
+    assert decode(good_desc(), max_ctx=2048, ws=FAKE, ws_bytes=need - 1) == E.PA_ERR_WORKSPACE
+
+
+def reshape(k=FAKE, kp=2048, v=FAKE, vp=2048, slots=FAKE, T=4, kc=FAKE, kb=64 * 16 * 2048, kview=None, vc=FAKE,
+            vb=64 * 16 * 2048, vview=None, layer=0, bs=16, nb=64):
+    kview = kview or pa.dense_view(16, 8, 128).c()
+    vview = vview or pa.dense_view(16, 8, 128).c()
+    return L._lib.pa_reshape_and_cache(k, kp, v, vp, slots, T, kc, kb, kview, vc, vb, vview, layer, bs, nb, None)
+
+
+def test_reshape_and_cache_status_codes():
+    E = L
+    assert reshape(T=0) == E.PA_OK
+    assert reshape(T=-1) == E.PA_ERR_INVALID_ARGUMENT
+    assert reshape(k=None) == E.PA_ERR_NULL_POINTER
+    assert reshape(slots=None) == E.PA_ERR_NULL_POINTER
+    assert reshape(vc=None) == E.PA_ERR_NULL_POINTER
+    assert reshape(kb=64 * 16 * 2048 - 4) == E.PA_ERR_VIEW_OUT_OF_RANGE
+    assert reshape(kp=1024) == E.PA_ERR_INVALID_ARGUMENT                     # pitch < row
+    assert reshape(k=FAKE + 2) == E.PA_ERR_MISALIGNED
+    assert reshape(kview=L.pa_cache_view(0, 0, 16 * 2048, 2048, 1)) == E.PA_ERR_INVALID_ARGUMENT  # reserved
+    assert reshape(kview=L.pa_cache_view(0, 0, 1000, 2048, 0)) == E.PA_ERR_INVALID_ARGUMENT  # page > block stride
+    # Indexer rows (132 B) are 4-byte aligned only: that is accepted by validation (not launched here).
+    assert reshape(kview=L.pa_cache_view(2, 0, 16 * 132, 132, 0), kb=10 ** 6) == E.PA_ERR_MISALIGNED
+
+
+def test_prefill_and_workspace_queries_reject_null_desc():
+    assert L._lib.pa_prefill_workspace_bytes(None, 1, 1, 1, 1) == 0
+    assert L._lib.pa_decode_workspace_bytes(None, 1, 1) == 0

@@ -102,7 +102,7 @@ typedef struct pa_attn_desc {
                                      K/V head h / (num_q_heads/num_kv_heads) ([MEM] §3.2). MLA: 1 */
     int32_t qk_dim;               /* dense: head_dim (64, 128 or 256). MLA: 576 */
     int32_t v_dim;                /* dense: == qk_dim. MLA: 512 */
-    int32_t block_size;           /* tokens per block: a multiple of 16, at most 256 */
+    int32_t block_size;           /* tokens per block: a power of two from 16 to 256 */
     int32_t layer;                /* layer index applied to the views' layer_stride */
     int32_t partition_size;       /* decode only: tokens per split-context partition; 0 lets the
                                      library choose; otherwise a positive multiple of block_size */
@@ -171,7 +171,7 @@ size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int
  *   context_lens   device int32 [num_seqs]: tokens to attend, the current one included (the caller
  *                  writes it first). 0 gives an output of 0.
  *   max_context_len  host upper bound of context_lens; sizes the grid.
- *   scale          softmax scale (e.g. 1/sqrt(qk_dim)).
+ *   scale          softmax scale, finite and >= 0 (e.g. 1/sqrt(qk_dim)).
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...) bytes (may be NULL when
  *                  that is 0). Its contents on entry do not matter.
  * Alignment: q, out, cache bases, view offsets, strides and row_bytes: 16 bytes.

@@ -44,7 +44,14 @@ bool view_aligned(const pa_cache_view& v, int32_t layer, int64_t a) {
 constexpr int32_t kMaxBlockSize = 256;
 constexpr int32_t kDefaultPartition = 512;
 
-bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= kMaxBlockSize && bs % 16 == 0; }
+// Block sizes are powers of two from 16 to 256, so that token -> (block, row) is a shift and a mask.
+bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= kMaxBlockSize && (bs & (bs - 1)) == 0; }
+
+int32_t log2_int(int32_t v) {
+    int32_t r = 0;
+    while ((1 << r) < v) ++r;
+    return r;
+}
 
 // Tokens per split-context partition. A requested size is a multiple of block_size; partitions are
 // capped at 64 blocks, because a partition's block ids are held one per lane of a wave.
@@ -166,7 +173,7 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
     if (num_seqs < 0 || max_context_len < 0) return PA_ERR_INVALID_ARGUMENT;
     if (num_seqs == 0) return PA_OK;
     if (!out || !q || !k_cache || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
-    if (bt_stride <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+    if (bt_stride <= 0 || !std::isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARGUMENT;
     const pa_attn_desc& d = *desc;
     if (d.kv_format == PA_KV_MLA656_E4M3) return PA_ERR_UNSUPPORTED;
     int32_t st = check_dense_desc(d);
@@ -204,6 +211,7 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
     p.num_q_heads = d.num_q_heads;
     p.num_kv_heads = d.num_kv_heads;
     p.block_size = d.block_size;
+    p.tiles_per_block_log2 = log2_int(d.block_size / 16);
     p.partition_tokens = P;
     p.max_parts = max_parts;
     p.max_context_len = max_context_len;

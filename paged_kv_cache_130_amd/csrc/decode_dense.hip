@@ -37,12 +37,26 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <bool BF16, int D, int G>
 struct Tile {
     static constexpr int LPR = D / 8;     // lanes per row
     static constexpr int RPL = 64 / LPR;  // rows per wave-wide load
     static constexpr int NL = 16 / RPL;   // loads per 16-token tile
 };
+
+// Online softmax with a lazily moved reference: each row group keeps a reference m (log2 domain)
+// and accumulates p = 2^(s*scale*log2e - m). The reference moves only when a tile's maximum
+// exceeds it by more than kRescaleSlack, so p <= 2^kRescaleSlack and the accumulators stay well
+// inside fp32 range. When no lane of the wave needs to move (the common case after the first
+// tile), the rescale of l and acc is skipped entirely. The result is the same softmax: every p and
+// the accumulators always share the same reference.
+constexpr float kRescaleSlack = 8.f;
+
+// v_perm_b32 selectors: low 16-bit halves of (a, b) -> (a.lo, b.lo); high halves -> (a.hi, b.hi).
+constexpr uint32_t kSelLo = 0x05040100u;
+constexpr uint32_t kSelHi = 0x07060302u;
 
 template <bool BF16, int D, int G, bool MASK>
 __device__ __forceinline__ void tile_step(const uint4 (&kr)[Tile<BF16, D, G>::NL],
@@ -51,6 +65,7 @@ __device__ __forceinline__ void tile_step(const uint4 (&kr)[Tile<BF16, D, G>::NL
                                           float scale_log2) {
     using T = Tile<BF16, D, G>;
     constexpr int NL = T::NL, RPL = T::RPL, LPR = T::LPR;
+    // Raw scores q.k of this row group's NL tokens, summed over the LPR lanes of the row.
     float sc[G][NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -60,54 +75,73 @@ __device__ __forceinline__ void tile_step(const uint4 (&kr)[Tile<BF16, D, G>::NL
             float d1 = dot2acc<BF16>(qr[g][1], kr[i].y, 0.f);
             d0 = dot2acc<BF16>(qr[g][2], kr[i].z, d0);
             d1 = dot2acc<BF16>(qr[g][3], kr[i].w, d1);
-            sc[g][i] = group_sum<LPR>(d0 + d1) * scale_log2;
+            sc[g][i] = group_sum<LPR>(d0 + d1);
         }
     }
-    if constexpr (MASK) {
+    bool ok[NL];
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const bool ok = r + i * RPL < nvalid;
-#pragma unroll
-            for (int g = 0; g < G; ++g) sc[g][i] = ok ? sc[g][i] : kNegInf;
-        }
-    }
-    float pr[G][NL];
+    for (int i = 0; i < NL; ++i) ok[i] = !MASK || (r + i * RPL < nvalid);
+    // Move the reference where this tile's maximum is too far above it.
+    bool need_any = false;
+    float tmax[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        float mx = m[g];
+        float mx = kNegInf;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) mx = fmaxf(mx, sc[g][i]);
-        const float ms = (mx == kNegInf) ? 0.f : mx;
-        const float alpha = fast_exp2(m[g] - ms);
-        float ps = 0.f;
+        for (int i = 0; i < NL; ++i) mx = ok[i] ? fmaxf(mx, sc[g][i]) : mx;
+        tmax[g] = mx * scale_log2;  // scale >= 0, so the maximum commutes with the scaling
+        need_any |= tmax[g] > m[g] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const bool need = tmax[g] > m[g] + kRescaleSlack;
+            const float mnew = need ? tmax[g] : m[g];
+            const float alpha = need ? fast_exp2(m[g] - mnew) : 1.f;  // m = -inf gives 0
+            l[g] *= alpha;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[g][d] *= alpha;
+            m[g] = mnew;
+        }
+    }
+    // p for every (head, token); masked tokens get exactly 0.
+    float pr[G][NL];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            pr[g][i] = fast_exp2(sc[g][i] - ms);
-            ps += pr[g][i];
+            const float e = fast_exp2(fmaf(sc[g][i], scale_log2, -m[g]));
+            pr[g][i] = ok[i] ? e : 0.f;
+            l[g] += pr[g][i];
         }
-        l[g] = l[g] * alpha + ps;
-        m[g] = mx;
+    // PV over token pairs with dot2: (v_a[d], v_b[d]) . (p_a, p_b), fp32 accumulation. V words of
+    // masked tokens are zeroed first: rows past the context may hold NaN, and 0 * NaN = NaN.
 #pragma unroll
-        for (int d = 0; d < 8; ++d) acc[g][d] *= alpha;
-    }
+    for (int i = 0; i < NL; i += 2) {
+        uint32_t wa[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+        uint32_t wb[4] = {vr[i + 1].x, vr[i + 1].y, vr[i + 1].z, vr[i + 1].w};
+        if constexpr (MASK) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-        float vf[8];
+            for (int k = 0; k < 4; ++k) {
+                wa[k] = ok[i] ? wa[k] : 0u;
+                wb[k] = ok[i + 1] ? wb[k] : 0u;
+            }
+        }
+        uint32_t lo[4], hi[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            vf[2 * k] = lo_f32<BF16>(w[k]);
-            vf[2 * k + 1] = hi_f32<BF16>(w[k]);
-        }
-        if constexpr (MASK) {
-            const bool ok = r + i * RPL < nvalid;
-#pragma unroll
-            for (int d = 0; d < 8; ++d) vf[d] = ok ? vf[d] : 0.f;  // rows past the context may hold NaN
+            lo[k] = __builtin_amdgcn_perm(wb[k], wa[k], kSelLo);
+            hi[k] = __builtin_amdgcn_perm(wb[k], wa[k], kSelHi);
         }
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g) {
+            const uint32_t pp = pack2<BF16>(pr[g][i], pr[g][i + 1]);
 #pragma unroll
-            for (int d = 0; d < 8; ++d) acc[g][d] = fmaf(pr[g][i], vf[d], acc[g][d]);
+            for (int k = 0; k < 4; ++k) {
+                acc[g][2 * k] = dot2acc<BF16>(pp, lo[k], acc[g][2 * k]);
+                acc[g][2 * k + 1] = dot2acc<BF16>(pp, hi[k], acc[g][2 * k + 1]);
+            }
+        }
     }
 }
 
@@ -118,18 +152,51 @@ __device__ __forceinline__ int clamp_context(int ctx, const DenseDecodeParams& p
     return (int)max((int64_t)0, min((int64_t)ctx, cap));
 }
 
-// Walks 16-token tiles inside blocks: (logical block relative to the partition, offset).
-struct TileCursor {
-    int lb;
-    int off;
-    __device__ __forceinline__ void advance(int bs) {
-        off += 16;
-        if (off == bs) {
-            off = 0;
-            ++lb;
-        }
+// Partitions of sequence s (at least 1 when its context is non-empty, 0 when empty... but an empty
+// context still owns one work item, which writes the zero output).
+__device__ __forceinline__ int parts_of(int s, const DenseDecodeParams& p) {
+    const int ctx = clamp_context(p.context_lens[s], p);
+    return ctx == 0 ? 1 : (ctx + p.partition_tokens - 1) / p.partition_tokens;
+}
+
+// Sum over the wave of min(nparts(s), cap) for all sequences (cap = max_parts gives the total).
+__device__ __forceinline__ int count_below(int cap, const DenseDecodeParams& p, int lane) {
+    int c = 0;
+    for (int s = lane; s < p.num_seqs; s += 64) c += min(parts_of(s, p), cap);
+    return __builtin_amdgcn_readfirstlane((int)group_sum<64>((float)c));
+}
+
+// Work item w of the partition-major list -> (sequence, partition). Returns false past the end.
+// C(q) = sum_s min(nparts(s), q) counts the items of partitions below q; item w lies in the partition
+// p with C(p) <= w < C(p+1), and is the (w - C(p))-th sequence (in order) that has more than p
+// partitions. Counts stay far below 2^24, so the float reductions are exact.
+__device__ __forceinline__ bool find_work(int w, const DenseDecodeParams& p, int& s_out, int& part_out) {
+    const int lane = threadIdx.x & 63;
+    if (w >= count_below(p.max_parts, p, lane)) return false;
+    int lo = 0, hi = p.max_parts;  // C(lo) <= w < C(hi)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (count_below(mid, p, lane) <= w) lo = mid;
+        else hi = mid;
     }
-};
+    int r = w - count_below(lo, p, lane);  // rank among sequences with more than lo partitions
+    for (int base = 0; base < p.num_seqs; base += 64) {
+        const int s = base + lane;
+        const bool has = s < p.num_seqs && parts_of(s, p) > lo;
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(has);
+        const int cnt = __builtin_popcountll(mask);
+        if (r < cnt) {
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(has && below == r);
+            s_out = base + __builtin_ctzll(hit);
+            part_out = lo;
+            return true;
+        }
+        r -= cnt;
+    }
+    return false;
+}
 
 }  // namespace
 
@@ -137,21 +204,22 @@ template <bool BF16, int D, int G>
 __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) {
     using T = Tile<BF16, D, G>;
     constexpr int LPR = T::LPR, RPL = T::RPL, NL = T::NL;
-    const int wave = threadIdx.x >> 6;
+    // Everything per item is wave-uniform; readfirstlane tells the compiler so, which keeps the
+    // item's control flow on scalar registers and the loop free of exec-mask branches.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r = lane / LPR;
     const int c = lane % LPR;
 
-    const int item = xcd_linear_block(blockIdx.x, gridDim.x) * 4 + wave;
-    const int per_head = p.num_seqs * p.max_parts;
-    if (item >= p.num_kv_heads * per_head) return;
-    const int kvh = item / per_head;
-    const int rem = item - kvh * per_head;
-    const int s = rem / p.max_parts;
-    const int part = rem - s * p.max_parts;
-
+    // Compact, partition-major work list: (partition p, sequence s) pairs with p < nparts(s), ordered by p
+    // then s, and the KV head fastest. Full-length partitions are dispatched first and the ragged tails
+    // of long sequences last, with no empty slots in between; waves past the end exit at once.
+    const int item = blockIdx.x * 4 + wave;
+    const int kvh = item % p.num_kv_heads;
+    int s, part;
+    if (!find_work(item / p.num_kv_heads, p, s, part)) return;
     const int bs = p.block_size;
-    const int ctx = clamp_context(p.context_lens[s], p);
+    const int ctx = clamp_context(__builtin_amdgcn_readfirstlane(p.context_lens[s]), p);
     const int P = p.partition_tokens;
     const int nparts = (ctx + P - 1) / P;
     const int hq0 = kvh * G;  // first query head of this group
@@ -184,15 +252,19 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
     }
 
     // Block ids of this partition: lane j holds logical block lb0 + j.
-    const int lb0 = tb / bs;
-    const int nblk = (te - tb + bs - 1) / bs;  // <= 64 by construction
+    const int lb0 = tb >> (p.tiles_per_block_log2 + 4);
+    const int nblk = (te - tb + bs - 1) >> (p.tiles_per_block_log2 + 4);  // <= 64 by construction
     const int32_t* bt = p.block_tables + (size_t)s * p.bt_stride;
     const int tbl = lane < nblk ? bt[lb0 + lane] : 0;
 
+    // Per-lane byte offset inside a tile (32-bit) and the uniform per-tile base (64-bit): loads take the
+    // scalar-base + vector-offset form.
     const int64_t krow = p.k_row_bytes, vrow = p.v_row_bytes;
-    const char* kbase = p.k + (int64_t)kvh * (D * 2) + c * 16 + r * krow;
-    const char* vbase = p.v + (int64_t)kvh * (D * 2) + c * 16 + r * vrow;
+    const uint32_t klane = (uint32_t)(kvh * (D * 2) + c * 16) + (uint32_t)r * (uint32_t)krow;
+    const uint32_t vlane = (uint32_t)(kvh * (D * 2) + c * 16) + (uint32_t)r * (uint32_t)vrow;
     const uint32_t nb = (uint32_t)p.num_blocks;
+    const int tpb_log2 = p.tiles_per_block_log2;  // block_size / 16 is a power of two
+    const int tpb_mask = (1 << tpb_log2) - 1;
 
     float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -204,47 +276,44 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
     }
 
     const int ntiles = (te - tb + 15) >> 4;
-    uint4 kA[NL], vA[NL], kB[NL], vB[NL];
-    // load cursor runs one tile ahead of the compute cursor (clamped at the last tile)
-    TileCursor ld{0, 0}, cp{0, 0};
-    int ld_tile = 0;
-
-    auto issue = [&](uint4 (&kk)[NL], uint4 (&vv)[NL]) {
-        int phys = __builtin_amdgcn_readlane(tbl, ld.lb);
-        phys = ((uint32_t)phys < nb) ? phys : 0;  // out-of-range ids are masked at compute time
-        const char* kp = kbase + (int64_t)phys * p.k_block_stride + (int64_t)ld.off * krow;
-        const char* vp = vbase + (int64_t)phys * p.v_block_stride + (int64_t)ld.off * vrow;
+    const int last = ntiles - 1;
+    // Tile j of the partition: logical block j >> tpb_log2 of the partition, rows (j & mask)*16 ...
+    auto block_of = [&](int j) {
+        const int phys = __builtin_amdgcn_readlane(tbl, j >> tpb_log2);
+        return phys;
+    };
+    auto load = [&](uint4 (&kk)[NL], uint4 (&vv)[NL], int j) {
+        int phys = block_of(j);
+        phys = ((uint32_t)phys < nb) ? phys : 0;  // an out-of-range id is masked when the tile is used
+        const int64_t row0 = (int64_t)((j & tpb_mask) << 4);
+        const char* kt = p.k + (int64_t)phys * p.k_block_stride + row0 * krow;
+        const char* vt = p.v + (int64_t)phys * p.v_block_stride + row0 * vrow;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            kk[i] = *reinterpret_cast<const uint4*>(kp + (int64_t)i * RPL * krow);
-            vv[i] = *reinterpret_cast<const uint4*>(vp + (int64_t)i * RPL * vrow);
-        }
-        if (ld_tile + 1 < ntiles) {
-            ld.advance(bs);
-            ++ld_tile;
+            // Nontemporal loads: each K/V row is read once per call, so it need not displace reused lines.
+            const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + (int64_t)i * RPL * krow + klane));
+            const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + (int64_t)i * RPL * vrow + vlane));
+            kk[i] = make_uint4(a.x, a.y, a.z, a.w);
+            vv[i] = make_uint4(b.x, b.y, b.z, b.w);
         }
     };
-    auto compute = [&](const uint4 (&kk)[NL], const uint4 (&vv)[NL], int tile) {
-        const int phys = __builtin_amdgcn_readlane(tbl, cp.lb);
-        const int t0 = tb + tile * 16;
-        int nvalid = min(16, te - t0);
-        if ((uint32_t)phys >= nb) nvalid = 0;
+    auto step = [&](const uint4 (&kk)[NL], const uint4 (&vv)[NL], int j) {
+        int nvalid = min(16, te - (tb + (j << 4)));
+        if ((uint32_t)block_of(j) >= nb) nvalid = 0;
         if (nvalid == 16)
             tile_step<BF16, D, G, false>(kk, vv, qr, m, l, acc, r, 16, p.scale_log2);
         else
             tile_step<BF16, D, G, true>(kk, vv, qr, m, l, acc, r, nvalid, p.scale_log2);
-        cp.advance(bs);
     };
 
-    issue(kA, vA);
-    int tile = 0;
-    for (;;) {
-        issue(kB, vB);
-        compute(kA, vA, tile);
-        if (++tile >= ntiles) break;
-        issue(kA, vA);
-        compute(kB, vB, tile);
-        if (++tile >= ntiles) break;
+    // Two register slots: the loads of tile j+1 are in flight while tile j is computed.
+    uint4 k0[NL], v0[NL], k1[NL], v1[NL];
+    load(k0, v0, 0);
+    for (int j = 0; j < ntiles; j += 2) {
+        load(k1, v1, min(j + 1, last));
+        step(k0, v0, j);
+        load(k0, v0, min(j + 2, last));
+        if (j + 1 < ntiles) step(k1, v1, j + 1);
     }
 
     // Merge the RPL row groups of the wave.
@@ -297,12 +366,12 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DenseDecodeParams p) {
     constexpr int DPL = D / 64;  // output values per lane
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int item = blockIdx.x * 4 + wave;  // = s * Hq + head
     if (item >= p.num_seqs * p.num_q_heads) return;
     const int s = item / p.num_q_heads;
-    const int ctx = clamp_context(p.context_lens[s], p);
+    const int ctx = clamp_context(__builtin_amdgcn_readfirstlane(p.context_lens[s]), p);
     const int nparts = (ctx + p.partition_tokens - 1) / p.partition_tokens;
     if (nparts <= 1) return;
     const float* ml = p.part_ml + (size_t)item * p.max_parts * 2;

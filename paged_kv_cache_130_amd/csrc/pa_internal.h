@@ -45,6 +45,7 @@ struct DenseDecodeParams {
     int32_t num_seqs;
     int32_t num_q_heads, num_kv_heads;
     int32_t block_size;
+    int32_t tiles_per_block_log2;  // log2(block_size / 16)
     int32_t partition_tokens;  // multiple of block_size, <= 64 * block_size
     int32_t max_parts;         // ceil(max_context_len / partition_tokens)
     int32_t max_context_len;   // clamp for context_lens

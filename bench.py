@@ -31,7 +31,7 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("decode_dense.hip", "pa_device.h", "pa_internal.h", "api.hip"):
+    for f in ("decode_dense.hip", "decode_mfma.hip", "decode_common.h", "pa_device.h", "pa_internal.h", "api.hip"):
         with open(os.path.join(ROOT, "paged_kv_cache_130_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -99,7 +99,8 @@ typedef struct pa_attn_desc {
     int32_t kv_format;            /* pa_kv_format */
     int32_t num_q_heads;          /* query heads */
     int32_t num_kv_heads;         /* K/V heads; num_q_heads % num_kv_heads == 0. Query head h reads
-                                     K/V head h / (num_q_heads/num_kv_heads) ([MEM] §3.2). MLA: 1 */
+                                     K/V head h / (num_q_heads/num_kv_heads) ([MEM] §3.2). Dense:
+                                     group size 1..16 at head_dim 128, else 1, 2, 4 or 8. MLA: 1 */
     int32_t qk_dim;               /* dense: head_dim (64, 128 or 256). MLA: 576 */
     int32_t v_dim;                /* dense: == qk_dim. MLA: 512 */
     int32_t block_size;           /* tokens per block: a power of two from 16 to 256 */

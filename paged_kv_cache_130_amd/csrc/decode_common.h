@@ -1,0 +1,87 @@
+// Work mapping shared by the decode kernels: context clamping and the compact, partition-major
+// list of (partition, sequence) items. Included only by .hip kernel files.
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr float kNegInf = -__builtin_inff();
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Online softmax with a lazily moved reference: each row keeps a reference m (log2 domain) and
+// accumulates p = 2^(s*scale*log2e - m). The reference moves only when a tile's maximum exceeds it
+// by more than kRescaleSlack, so p <= 2^kRescaleSlack and the accumulators stay well inside fp32
+// range. When no lane of the wave needs to move (the common case after the first tile), the rescale
+// of l and the accumulators is skipped. The result is the same softmax: every p and the
+// accumulators always share the same reference.
+constexpr float kRescaleSlack = 8.f;
+
+// v_perm_b32 selectors: low 16-bit halves of (a, b) -> (a.lo, b.lo); high halves -> (a.hi, b.hi).
+constexpr uint32_t kSelLo = 0x05040100u;
+constexpr uint32_t kSelHi = 0x07060302u;
+
+// 16 bytes through a nontemporal load: each K/V row is read once per call, so it should not displace
+// lines that are reused.
+__device__ __forceinline__ uint4 load_nt16(const char* ptr) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+    return make_uint4(a.x, a.y, a.z, a.w);
+}
+
+// Context length bounded to [0, min(max_context_len, bt_stride * block_size)], so that no read
+// goes past the block table row.
+__device__ __forceinline__ int clamp_context(int ctx, const DenseDecodeParams& p) {
+    const int64_t cap = min((int64_t)p.max_context_len, (int64_t)p.bt_stride * p.block_size);
+    return (int)max((int64_t)0, min((int64_t)ctx, cap));
+}
+
+// Work items of sequence s: one per partition; an empty context still owns one item, which writes
+// the zero output.
+__device__ __forceinline__ int parts_of(int s, const DenseDecodeParams& p) {
+    const int ctx = clamp_context(p.context_lens[s], p);
+    return ctx == 0 ? 1 : (ctx + p.partition_tokens - 1) / p.partition_tokens;
+}
+
+// Sum over the wave of min(nparts(s), cap) for all sequences (cap = max_parts gives the total).
+__device__ __forceinline__ int count_below(int cap, const DenseDecodeParams& p, int lane) {
+    int c = 0;
+    for (int s = lane; s < p.num_seqs; s += 64) c += min(parts_of(s, p), cap);
+    return __builtin_amdgcn_readfirstlane((int)group_sum<64>((float)c));
+}
+
+// Work item w of the partition-major list -> (sequence, partition). Returns false past the end.
+// C(q) = sum_s min(nparts(s), q) counts the items of partitions below q; item w lies in the partition
+// p with C(p) <= w < C(p+1), and is the (w - C(p))-th sequence (in order) that has more than p
+// partitions. Counts stay far below 2^24, so the float reductions are exact.
+__device__ __forceinline__ bool find_work(int w, const DenseDecodeParams& p, int& s_out, int& part_out) {
+    const int lane = threadIdx.x & 63;
+    if (w >= count_below(p.max_parts, p, lane)) return false;
+    int lo = 0, hi = p.max_parts;  // C(lo) <= w < C(hi)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (count_below(mid, p, lane) <= w) lo = mid;
+        else hi = mid;
+    }
+    int r = w - count_below(lo, p, lane);  // rank among sequences with more than lo partitions
+    for (int base = 0; base < p.num_seqs; base += 64) {
+        const int s = base + lane;
+        const bool has = s < p.num_seqs && parts_of(s, p) > lo;
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(has);
+        const int cnt = __builtin_popcountll(mask);
+        if (r < cnt) {
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(has && below == r);
+            s_out = base + __builtin_ctzll(hit);
+            part_out = lo;
+            return true;
+        }
+        r -= cnt;
+    }
+    return false;
+}
+
+
+}  // namespace pa

@@ -28,16 +28,12 @@
 //        out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p
 //    (scores are kept in the log2 domain: s * scale * log2(e)).
 
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "decode_common.h"
 
 namespace pa {
 
 namespace {
 
-constexpr float kNegInf = -__builtin_inff();
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <bool BF16, int D, int G>
 struct Tile {
@@ -45,18 +41,6 @@ struct Tile {
     static constexpr int RPL = 64 / LPR;  // rows per wave-wide load
     static constexpr int NL = 16 / RPL;   // loads per 16-token tile
 };
-
-// Online softmax with a lazily moved reference: each row group keeps a reference m (log2 domain)
-// and accumulates p = 2^(s*scale*log2e - m). The reference moves only when a tile's maximum
-// exceeds it by more than kRescaleSlack, so p <= 2^kRescaleSlack and the accumulators stay well
-// inside fp32 range. When no lane of the wave needs to move (the common case after the first
-// tile), the rescale of l and acc is skipped entirely. The result is the same softmax: every p and
-// the accumulators always share the same reference.
-constexpr float kRescaleSlack = 8.f;
-
-// v_perm_b32 selectors: low 16-bit halves of (a, b) -> (a.lo, b.lo); high halves -> (a.hi, b.hi).
-constexpr uint32_t kSelLo = 0x05040100u;
-constexpr uint32_t kSelHi = 0x07060302u;
 
 template <bool BF16, int D, int G, bool MASK>
 __device__ __forceinline__ void tile_step(const uint4 (&kr)[Tile<BF16, D, G>::NL],
@@ -145,59 +129,6 @@ __device__ __forceinline__ void tile_step(const uint4 (&kr)[Tile<BF16, D, G>::NL
     }
 }
 
-// Context length bounded to [0, min(max_context_len, bt_stride * block_size)], so that no read
-// goes past the block table row.
-__device__ __forceinline__ int clamp_context(int ctx, const DenseDecodeParams& p) {
-    const int64_t cap = min((int64_t)p.max_context_len, (int64_t)p.bt_stride * p.block_size);
-    return (int)max((int64_t)0, min((int64_t)ctx, cap));
-}
-
-// Partitions of sequence s (at least 1 when its context is non-empty, 0 when empty... but an empty
-// context still owns one work item, which writes the zero output).
-__device__ __forceinline__ int parts_of(int s, const DenseDecodeParams& p) {
-    const int ctx = clamp_context(p.context_lens[s], p);
-    return ctx == 0 ? 1 : (ctx + p.partition_tokens - 1) / p.partition_tokens;
-}
-
-// Sum over the wave of min(nparts(s), cap) for all sequences (cap = max_parts gives the total).
-__device__ __forceinline__ int count_below(int cap, const DenseDecodeParams& p, int lane) {
-    int c = 0;
-    for (int s = lane; s < p.num_seqs; s += 64) c += min(parts_of(s, p), cap);
-    return __builtin_amdgcn_readfirstlane((int)group_sum<64>((float)c));
-}
-
-// Work item w of the partition-major list -> (sequence, partition). Returns false past the end.
-// C(q) = sum_s min(nparts(s), q) counts the items of partitions below q; item w lies in the partition
-// p with C(p) <= w < C(p+1), and is the (w - C(p))-th sequence (in order) that has more than p
-// partitions. Counts stay far below 2^24, so the float reductions are exact.
-__device__ __forceinline__ bool find_work(int w, const DenseDecodeParams& p, int& s_out, int& part_out) {
-    const int lane = threadIdx.x & 63;
-    if (w >= count_below(p.max_parts, p, lane)) return false;
-    int lo = 0, hi = p.max_parts;  // C(lo) <= w < C(hi)
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (count_below(mid, p, lane) <= w) lo = mid;
-        else hi = mid;
-    }
-    int r = w - count_below(lo, p, lane);  // rank among sequences with more than lo partitions
-    for (int base = 0; base < p.num_seqs; base += 64) {
-        const int s = base + lane;
-        const bool has = s < p.num_seqs && parts_of(s, p) > lo;
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(has);
-        const int cnt = __builtin_popcountll(mask);
-        if (r < cnt) {
-            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(has && below == r);
-            s_out = base + __builtin_ctzll(hit);
-            part_out = lo;
-            return true;
-        }
-        r -= cnt;
-    }
-    return false;
-}
-
 }  // namespace
 
 template <bool BF16, int D, int G>
@@ -282,19 +213,22 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
         const int phys = __builtin_amdgcn_readlane(tbl, j >> tpb_log2);
         return phys;
     };
+    // Tile j > last is a dummy: every lane reads the same 16 bytes of this item's (cached) query, so
+    // the unconditional prefetch after the last tile costs no HBM traffic.
+    const char* dummy = reinterpret_cast<const char*>(qsrc - c * 8);
     auto load = [&](uint4 (&kk)[NL], uint4 (&vv)[NL], int j) {
-        int phys = block_of(j);
+        const bool real = j <= last;
+        int phys = block_of(real ? j : last);
         phys = ((uint32_t)phys < nb) ? phys : 0;  // an out-of-range id is masked when the tile is used
         const int64_t row0 = (int64_t)((j & tpb_mask) << 4);
-        const char* kt = p.k + (int64_t)phys * p.k_block_stride + row0 * krow;
-        const char* vt = p.v + (int64_t)phys * p.v_block_stride + row0 * vrow;
+        const char* kt = real ? p.k + (int64_t)phys * p.k_block_stride + row0 * krow : dummy;
+        const char* vt = real ? p.v + (int64_t)phys * p.v_block_stride + row0 * vrow : dummy;
+        const int64_t kstep = real ? (int64_t)RPL * krow : 0, vstep = real ? (int64_t)RPL * vrow : 0;
+        const uint32_t ko = real ? klane : 0u, vo = real ? vlane : 0u;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            // Nontemporal loads: each K/V row is read once per call, so it need not displace reused lines.
-            const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + (int64_t)i * RPL * krow + klane));
-            const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + (int64_t)i * RPL * vrow + vlane));
-            kk[i] = make_uint4(a.x, a.y, a.z, a.w);
-            vv[i] = make_uint4(b.x, b.y, b.z, b.w);
+            kk[i] = load_nt16(kt + i * kstep + ko);
+            vv[i] = load_nt16(vt + i * vstep + vo);
         }
     };
     auto step = [&](const uint4 (&kk)[NL], const uint4 (&vv)[NL], int j) {
@@ -310,9 +244,9 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
     uint4 k0[NL], v0[NL], k1[NL], v1[NL];
     load(k0, v0, 0);
     for (int j = 0; j < ntiles; j += 2) {
-        load(k1, v1, min(j + 1, last));
+        load(k1, v1, j + 1);
         step(k0, v0, j);
-        load(k0, v0, min(j + 2, last));
+        load(k0, v0, j + 2);
         if (j + 1 < ntiles) step(k1, v1, j + 1);
     }
 
@@ -409,14 +343,11 @@ namespace {
 template <bool BF16, int D, int G>
 hipError_t launch_typed(const DenseDecodeParams& p, hipStream_t stream) {
     const int64_t items = (int64_t)p.num_kv_heads * p.num_seqs * p.max_parts;
-    int64_t wgs = (items + 3) / 4;
-    wgs = (wgs + 7) / 8 * 8;
+    const int64_t wgs = (items + 3) / 4;
     hipLaunchKernelGGL((decode_dense_kernel<BF16, D, G>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.max_parts <= 1) return e;
-    const int64_t red = ((int64_t)p.num_seqs * p.num_q_heads + 3) / 4;
-    hipLaunchKernelGGL((decode_reduce_kernel<BF16, D>), dim3((unsigned)red), dim3(256), 0, stream, p);
-    return hipGetLastError();
+    return launch_decode_reduce(p, stream);
 }
 
 template <bool BF16, int D>
@@ -442,8 +373,29 @@ hipError_t launch_dim(const DenseDecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_decode_reduce(const DenseDecodeParams& p, hipStream_t stream) {
+    const int64_t red = ((int64_t)p.num_seqs * p.num_q_heads + 3) / 4;
+    if (p.is_bf16) {
+        switch (p.head_dim) {
+            case 64: hipLaunchKernelGGL((decode_reduce_kernel<true, 64>), dim3((unsigned)red), dim3(256), 0, stream, p); break;
+            case 128: hipLaunchKernelGGL((decode_reduce_kernel<true, 128>), dim3((unsigned)red), dim3(256), 0, stream, p); break;
+            default: hipLaunchKernelGGL((decode_reduce_kernel<true, 256>), dim3((unsigned)red), dim3(256), 0, stream, p); break;
+        }
+    } else {
+        switch (p.head_dim) {
+            case 64: hipLaunchKernelGGL((decode_reduce_kernel<false, 64>), dim3((unsigned)red), dim3(256), 0, stream, p); break;
+            case 128: hipLaunchKernelGGL((decode_reduce_kernel<false, 128>), dim3((unsigned)red), dim3(256), 0, stream, p); break;
+            default: hipLaunchKernelGGL((decode_reduce_kernel<false, 256>), dim3((unsigned)red), dim3(256), 0, stream, p); break;
+        }
+    }
+    return hipGetLastError();
+}
+
+// Grouped heads at head_dim 128 run on the matrix cores (decode_mfma.hip); single heads and the other
+// head sizes run on the VALU kernel above.
 hipError_t launch_decode_dense(const DenseDecodeParams& p, hipStream_t stream) {
     if (p.num_seqs <= 0) return hipSuccess;
+    if (p.head_dim == 128 && p.group >= 2) return launch_decode_mfma(p, stream);
     return p.is_bf16 ? launch_dim<true>(p, stream) : launch_dim<false>(p, stream);
 }
 

@@ -27,7 +27,7 @@ struct CacheWriteParams {
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
-// Dense paged decode (fp16 / bf16 rows, head_dim 64 / 128 / 256, group <= 8)
+// Dense paged decode (fp16 / bf16 rows, head_dim 64 / 128 / 256; group 1, 2, 4, 8, or 2..16 at head_dim 128)
 // ---------------------------------------------------------------------------
 struct DenseDecodeParams {
     void* out;                 // [num_seqs, Hq, D]
@@ -54,6 +54,8 @@ struct DenseDecodeParams {
     int32_t head_dim;
     int32_t group;             // Hq / Hkv
 };
-hipError_t launch_decode_dense(const DenseDecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_dense(const DenseDecodeParams& p, hipStream_t stream);   // picks the kernel below
+hipError_t launch_decode_mfma(const DenseDecodeParams& p, hipStream_t stream);    // head_dim 128, group 2..16
+hipError_t launch_decode_reduce(const DenseDecodeParams& p, hipStream_t stream);  // partition merge
 
 }  // namespace pa

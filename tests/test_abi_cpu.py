@@ -59,7 +59,8 @@ def test_decode_status_codes():
     assert decode(good_desc(), scale=float("nan")) == E.PA_ERR_INVALID_ARGUMENT
     assert decode(good_desc(), scale=-0.5) == E.PA_ERR_INVALID_ARGUMENT
     assert decode(good_desc(num_kv_heads=3)) == E.PA_ERR_INVALID_ARGUMENT   # 8 % 3 != 0
-    assert decode(good_desc(num_q_heads=40, num_kv_heads=8)) == E.PA_ERR_UNSUPPORTED  # group 5
+    assert decode(good_desc(num_q_heads=34, num_kv_heads=2)) == E.PA_ERR_UNSUPPORTED  # group 17
+    assert decode(good_desc(num_q_heads=24, num_kv_heads=8, qk_dim=64, v_dim=64)) == E.PA_ERR_UNSUPPORTED
     assert decode(good_desc(qk_dim=96, v_dim=96)) == E.PA_ERR_UNSUPPORTED
     assert decode(good_desc(v_dim=64)) == E.PA_ERR_INVALID_ARGUMENT
     assert decode(good_desc(block_size=8)) == E.PA_ERR_UNSUPPORTED

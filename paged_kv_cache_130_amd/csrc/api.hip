@@ -226,12 +226,13 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
 
 size_t pa_prefill_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t total_q,
                                   int32_t max_query_len, int32_t max_seq_len) {
-    (void)desc;
-    (void)num_seqs;
     (void)total_q;
     (void)max_query_len;
-    (void)max_seq_len;
-    return 0;
+    if (!desc || num_seqs <= 0 || max_seq_len <= 0) return 0;
+    if (desc->kv_format != PA_KV_F16 && desc->kv_format != PA_KV_BF16) return 0;
+    if (!block_size_ok(desc->block_size)) return 0;
+    // The decode rows (query length 1) of the call use split-context partials.
+    return dense_decode_ws(*desc, num_seqs, max_seq_len);
 }
 
 int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -239,10 +240,96 @@ int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const vo
                          const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q, int32_t max_query_len,
                          int32_t max_seq_len, float scale, const pa_attn_desc* desc, void* workspace,
                          size_t workspace_bytes, void* stream) {
-    (void)out; (void)q; (void)k_cache; (void)v_cache; (void)block_tables; (void)bt_stride; (void)seq_lens;
-    (void)query_start_loc; (void)num_seqs; (void)total_q; (void)max_query_len; (void)max_seq_len; (void)scale;
-    (void)desc; (void)workspace; (void)workspace_bytes; (void)stream;
-    return PA_ERR_UNSUPPORTED;
+    if (!desc) return PA_ERR_NULL_POINTER;
+    if (num_seqs < 0 || total_q < 0 || max_query_len < 0 || max_seq_len < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_seqs == 0 || total_q == 0) return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc)
+        return PA_ERR_NULL_POINTER;
+    if (bt_stride <= 0 || !std::isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARGUMENT;
+    const pa_attn_desc& d = *desc;
+    if (d.kv_format == PA_KV_MLA656_E4M3) return PA_ERR_UNSUPPORTED;
+    int32_t st = check_dense_desc(d);
+    if (st != PA_OK) return st;
+    if (d.qk_dim != 128) return PA_ERR_UNSUPPORTED;  // causal chunks are implemented for head_dim 128
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4))
+        return PA_ERR_MISALIGNED;
+    const size_t need = dense_decode_ws(d, num_seqs, max_seq_len);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return PA_ERR_MISALIGNED;
+    const int32_t P = effective_partition(d);
+    const int64_t max_parts64 = ((int64_t)max_seq_len + P - 1) / P;
+    const int32_t max_parts = max_parts64 < 1 ? 1 : (int32_t)max_parts64;
+    if ((int64_t)d.num_kv_heads * num_seqs * max_parts > 0x7FFFFFFFLL - 64) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)total_q * d.num_q_heads > 0x7FFFFFFFLL / 2) return PA_ERR_UNSUPPORTED;
+
+    const char* kb = static_cast<const char*>(k_cache) + d.k_view.offset + (int64_t)d.layer * d.k_view.layer_stride;
+    const char* vb = static_cast<const char*>(v_cache) + d.v_view.offset + (int64_t)d.layer * d.v_view.layer_stride;
+
+    // 1) Decode rows (query length 1): split-context decode over their whole context.
+    pa::DenseDecodeParams dp;
+    std::memset(&dp, 0, sizeof(dp));
+    dp.out = out;
+    dp.q = q;
+    dp.k = kb;
+    dp.v = vb;
+    dp.block_tables = block_tables;
+    dp.context_lens = seq_lens;
+    dp.query_start_loc = query_start_loc;
+    const int64_t n = (int64_t)num_seqs * d.num_q_heads * max_parts;
+    dp.part_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
+    dp.part_acc = need > 0 ? static_cast<float*>(workspace) + 2 * n : nullptr;
+    dp.k_block_stride = d.k_view.block_stride;
+    dp.v_block_stride = d.v_view.block_stride;
+    dp.num_blocks = d.num_blocks;
+    dp.k_row_bytes = d.k_view.row_bytes;
+    dp.v_row_bytes = d.v_view.row_bytes;
+    dp.bt_stride = bt_stride;
+    dp.num_seqs = num_seqs;
+    dp.num_q_heads = d.num_q_heads;
+    dp.num_kv_heads = d.num_kv_heads;
+    dp.block_size = d.block_size;
+    dp.tiles_per_block_log2 = log2_int(d.block_size / 16);
+    dp.partition_tokens = P;
+    dp.max_parts = max_parts;
+    dp.max_context_len = max_seq_len;
+    dp.scale_log2 = scale * 1.4426950408889634f;
+    dp.is_bf16 = d.kv_format == PA_KV_BF16;
+    dp.head_dim = d.qk_dim;
+    dp.group = d.num_q_heads / d.num_kv_heads;
+    st = hip_status(pa::launch_decode_dense(dp, static_cast<hipStream_t>(stream)));
+    if (st != PA_OK) return st;
+
+    // 2) Chunk rows (query length >= 2): causal attention over the paged context.
+    pa::PrefillParams pp;
+    std::memset(&pp, 0, sizeof(pp));
+    pp.out = out;
+    pp.q = q;
+    pp.k = kb;
+    pp.v = vb;
+    pp.block_tables = block_tables;
+    pp.seq_lens = seq_lens;
+    pp.query_start_loc = query_start_loc;
+    pp.k_block_stride = d.k_view.block_stride;
+    pp.v_block_stride = d.v_view.block_stride;
+    pp.num_blocks = d.num_blocks;
+    pp.k_row_bytes = d.k_view.row_bytes;
+    pp.v_row_bytes = d.v_view.row_bytes;
+    pp.bt_stride = bt_stride;
+    pp.num_seqs = num_seqs;
+    pp.num_q_heads = d.num_q_heads;
+    pp.num_kv_heads = d.num_kv_heads;
+    pp.block_size = d.block_size;
+    pp.tiles_per_block_log2 = log2_int(d.block_size / 16);
+    pp.max_seq_len = max_seq_len;
+    pp.max_query_len = max_query_len;
+    pp.scale_log2 = dp.scale_log2;
+    pp.is_bf16 = dp.is_bf16;
+    pp.group = dp.group;
+    pp.rows_per_item = 32;
+    pp.total_q = total_q;
+    if (max_query_len < 2) return PA_OK;
+    return hip_status(pa::launch_prefill_chunk(pp, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -38,10 +38,16 @@ __device__ __forceinline__ int clamp_context(int ctx, const DenseDecodeParams& p
 }
 
 // Work items of sequence s: one per partition; an empty context still owns one item, which writes
-// the zero output.
+// the zero output. In a mixed prefill call only single-row sequences have items.
 __device__ __forceinline__ int parts_of(int s, const DenseDecodeParams& p) {
+    if (p.query_start_loc != nullptr && p.query_start_loc[s + 1] - p.query_start_loc[s] != 1) return 0;
     const int ctx = clamp_context(p.context_lens[s], p);
     return ctx == 0 ? 1 : (ctx + p.partition_tokens - 1) / p.partition_tokens;
+}
+
+// Row of q / out that holds sequence s's (single) query token.
+__device__ __forceinline__ int query_row(int s, const DenseDecodeParams& p) {
+    return p.query_start_loc != nullptr ? __builtin_amdgcn_readfirstlane(p.query_start_loc[s]) : s;
 }
 
 // Sum over the wave of min(nparts(s), cap) for all sequences (cap = max_parts gives the total).

@@ -119,11 +119,16 @@ __device__ __forceinline__ void tile_step(const uint4 (&kr)[Tile<BF16, D, G>::NL
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const uint32_t pp = pack2<BF16>(pr[g][i], pr[g][i + 1]);
+            uint32_t pp, pl;
+            pack2_split<BF16>(pr[g][i], pr[g][i + 1], pp, pl);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 acc[g][2 * k] = dot2acc<BF16>(pp, lo[k], acc[g][2 * k]);
                 acc[g][2 * k + 1] = dot2acc<BF16>(pp, hi[k], acc[g][2 * k + 1]);
+                if constexpr (BF16) {
+                    acc[g][2 * k] = dot2acc<BF16>(pl, lo[k], acc[g][2 * k]);
+                    acc[g][2 * k + 1] = dot2acc<BF16>(pl, hi[k], acc[g][2 * k + 1]);
+                }
             }
         }
     }
@@ -154,6 +159,7 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
     const int P = p.partition_tokens;
     const int nparts = (ctx + P - 1) / P;
     const int hq0 = kvh * G;  // first query head of this group
+    const int qrow_idx = query_row(s, p);
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
 
     if (ctx == 0) {  // empty context: output 0
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
 #pragma unroll
             for (int g = 0; g < G; ++g)
                 if ((g % RPL) == r)
-                    *reinterpret_cast<uint4*>(out + ((size_t)s * p.num_q_heads + hq0 + g) * D + c * 8) =
+                    *reinterpret_cast<uint4*>(out + ((size_t)qrow_idx * p.num_q_heads + hq0 + g) * D + c * 8) =
                         make_uint4(0, 0, 0, 0);
         }
         return;
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
 
     // Query: 8 values of each of the G heads.
     uint32_t qr[G][4];
-    const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)s * p.num_q_heads + hq0) * D + c * 8;
+    const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)qrow_idx * p.num_q_heads + hq0) * D + c * 8;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const uint4 v = *reinterpret_cast<const uint4*>(qsrc + g * D);
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
             o.y = pack2<BF16>(acc[g][2] * inv, acc[g][3] * inv);
             o.z = pack2<BF16>(acc[g][4] * inv, acc[g][5] * inv);
             o.w = pack2<BF16>(acc[g][6] * inv, acc[g][7] * inv);
-            *reinterpret_cast<uint4*>(out + ((size_t)s * p.num_q_heads + hq0 + g) * D + c * 8) = o;
+            *reinterpret_cast<uint4*>(out + ((size_t)qrow_idx * p.num_q_heads + hq0 + g) * D + c * 8) = o;
         }
     } else {
 #pragma unroll
@@ -305,8 +311,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DenseDecodeParams p)
     const int item = blockIdx.x * 4 + wave;  // = s * Hq + head
     if (item >= p.num_seqs * p.num_q_heads) return;
     const int s = item / p.num_q_heads;
-    const int ctx = clamp_context(__builtin_amdgcn_readfirstlane(p.context_lens[s]), p);
-    const int nparts = (ctx + p.partition_tokens - 1) / p.partition_tokens;
+    const int head = item - s * p.num_q_heads;
+    const int nparts = __builtin_amdgcn_readfirstlane(parts_of(s, p));
     if (nparts <= 1) return;
     const float* ml = p.part_ml + (size_t)item * p.max_parts * 2;
     float M = kNegInf;
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DenseDecodeParams p)
         for (int k = 0; k < DPL; ++k) a[k] = fmaf(w, ap[(size_t)i * D + k], a[k]);
     }
     const float inv = 1.f / L;
-    uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + (size_t)item * D + lane * DPL;
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + ((size_t)query_row(s, p) * p.num_q_heads + head) * D + lane * DPL;
     if constexpr (DPL == 1) {
         out[0] = (uint16_t)(pack2<BF16>(a[0] * inv, 0.f) & 0xFFFFu);
     } else if constexpr (DPL == 2) {

@@ -27,41 +27,11 @@
 // their V rows are zeroed, partitions and their merge as in decode_dense.hip.
 
 #include "decode_common.h"
+#include "mfma_common.h"
 
 namespace pa {
 
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-template <bool BF16>
-__device__ __forceinline__ f32x4_t mfma_k32(uint4 a, uint4 b, f32x4_t c) {
-    if constexpr (BF16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                       c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
-                                                      0, 0, 0);
-}
-
-template <bool BF16>
-__device__ __forceinline__ f32x4_t mfma_k16(uint2 a, uint2 b, f32x4_t c) {
-    if constexpr (BF16)
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
-                                                         c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c,
-                                                     0, 0, 0);
-}
-
-constexpr int kD = 128;
-
-// Tile row held by MFMA A-row m (see the header comment).
-__device__ __forceinline__ int sigma(int m) { return (m >> 2) + 4 * (m & 3); }
 
 template <bool BF16>
 __device__ __forceinline__ void mfma_tile_step(const uint4 (&kk)[4], uint4 (&vv)[4], const uint4 (&qb)[4], float& m,
@@ -100,22 +70,17 @@ __device__ __forceinline__ void mfma_tile_step(const uint4 (&kk)[4], uint4 (&vv)
         pr[j] = ok[j] ? e : 0.f;
         l += pr[j];
     }
-    const uint2 A = make_uint2(pack2<BF16>(pr[0], pr[1]), pack2<BF16>(pr[2], pr[3]));
+    uint2 A, Alo;
+    pack2_split<BF16>(pr[0], pr[1], A.x, Alo.x);
+    pack2_split<BF16>(pr[2], pr[3], A.y, Alo.y);
 #pragma unroll
     for (int i = 0; i < 4; ++i)  // rows past the context may hold NaN, and 0 * NaN = NaN
         if (!ok[i]) vv[i] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? kSelHi : kSelLo;
-        uint32_t w0, w1, w2, w3;
-        switch (e >> 1) {
-            case 0: w0 = vv[0].x; w1 = vv[1].x; w2 = vv[2].x; w3 = vv[3].x; break;
-            case 1: w0 = vv[0].y; w1 = vv[1].y; w2 = vv[2].y; w3 = vv[3].y; break;
-            case 2: w0 = vv[0].z; w1 = vv[1].z; w2 = vv[2].z; w3 = vv[3].z; break;
-            default: w0 = vv[0].w; w1 = vv[1].w; w2 = vv[2].w; w3 = vv[3].w; break;
-        }
-        const uint2 B = make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
+        const uint2 B = v_operand(vv, e);
         O[e] = mfma_k16<BF16>(A, B, O[e]);
+        if constexpr (BF16) O[e] = mfma_k16<BF16>(Alo, B, O[e]);
     }
 }
 
@@ -139,12 +104,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DenseDecodeParams p) {
     const int P = p.partition_tokens;
     const int nparts = (ctx + P - 1) / P;
     const int hq0 = kvh * G;
+    const int qr = query_row(s, p);
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)s * p.num_q_heads + hq0) * kD;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)qr * p.num_q_heads + hq0) * kD;
 
     if (ctx == 0) {
         for (int h = g4; h < G; h += 4)
-            *reinterpret_cast<uint4*>(out + ((size_t)s * p.num_q_heads + hq0 + h) * kD + c * 8) = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(out + ((size_t)qr * p.num_q_heads + hq0 + h) * kD + c * 8) = make_uint4(0, 0, 0, 0);
         return;
     }
     if (part >= nparts) return;
@@ -227,7 +193,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DenseDecodeParams p) {
             o.y = pack2<BF16>(O[2][j] * inv, O[3][j] * inv);
             o.z = pack2<BF16>(O[4][j] * inv, O[5][j] * inv);
             o.w = pack2<BF16>(O[6][j] * inv, O[7][j] * inv);
-            *reinterpret_cast<uint4*>(out + ((size_t)s * p.num_q_heads + hq0 + h) * kD + c * 8) = o;
+            *reinterpret_cast<uint4*>(out + ((size_t)qr * p.num_q_heads + hq0 + h) * kD + c * 8) = o;
         } else {
             const size_t idx = ((size_t)s * p.num_q_heads + hq0 + h) * p.max_parts + part;
             float4* pa = reinterpret_cast<float4*>(p.part_acc + idx * kD + c * 8);

@@ -77,6 +77,18 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     }
 }
 
+// Probability pairs as 16-bit operands of the PV product. For fp16 one packed pair carries 11
+// significant bits, enough for the 2e-3 absolute tolerance. For bf16 one pair carries only 8, and a
+// weight rounded by 2^-9 of itself can move a short row's output by more than that. So bf16 pairs
+// come as hi + lo: hi = bf16(p), lo = bf16(p - hi), which holds p to about 2^-17. The caller
+// accumulates both into the same fp32 sum.
+template <bool BF16>
+__device__ __forceinline__ void pack2_split(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pack2<BF16>(a, b);
+    if constexpr (BF16) lo = pack2<true>(a - lo_f32<true>(hi), b - hi_f32<true>(hi));
+    else lo = 0u;
+}
+
 // Work-group index -> linear index such that consecutive linear indices run on the same XCD.
 // Work-groups are dispatched round-robin over the 8 XCDs of an MI355X, so group b lands on
 // XCD b % 8; giving each XCD a contiguous chunk keeps related work (same KV head) in one L2.

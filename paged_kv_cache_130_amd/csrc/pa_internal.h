@@ -36,6 +36,9 @@ struct DenseDecodeParams {
     const char* v;
     const int32_t* block_tables;
     const int32_t* context_lens;
+    const int32_t* query_start_loc;  // null for pa_decode. Otherwise sequence s's query is row
+                                     // query_start_loc[s], and only sequences with exactly one query
+                                     // row take part (the decode rows of a mixed prefill call).
     float* part_ml;            // [num_seqs, Hq, max_parts, 2]: running max (log2 domain), sum
     float* part_acc;           // [num_seqs, Hq, max_parts, D]: unnormalised accumulator
     int64_t k_block_stride, v_block_stride;
@@ -57,5 +60,34 @@ struct DenseDecodeParams {
 hipError_t launch_decode_dense(const DenseDecodeParams& p, hipStream_t stream);   // picks the kernel below
 hipError_t launch_decode_mfma(const DenseDecodeParams& p, hipStream_t stream);    // head_dim 128, group 2..16
 hipError_t launch_decode_reduce(const DenseDecodeParams& p, hipStream_t stream);  // partition merge
+
+// ---------------------------------------------------------------------------
+// Causal chunks over paged context (query length >= 2), head_dim 128, group 1..16
+// ---------------------------------------------------------------------------
+struct PrefillParams {
+    void* out;                 // [total_q, Hq, 128]
+    const void* q;             // [total_q, Hq, 128]
+    const char* k;             // cache base + view offset + layer * layer_stride
+    const char* v;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    const int32_t* query_start_loc;  // [num_seqs + 1]
+    int64_t k_block_stride, v_block_stride;
+    int64_t num_blocks;
+    int32_t k_row_bytes, v_row_bytes;
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t num_q_heads, num_kv_heads;
+    int32_t block_size;
+    int32_t tiles_per_block_log2;
+    int32_t max_seq_len;       // clamp for seq_lens
+    int32_t max_query_len;     // clamp for query lengths
+    float scale_log2;
+    int32_t is_bf16;
+    int32_t group;             // Hq / Hkv
+    int32_t rows_per_item;     // query rows (position x head) per wave
+    int32_t total_q;           // query rows of the call (bounds the grid)
+};
+hipError_t launch_prefill_chunk(const PrefillParams& p, hipStream_t stream);
 
 }  // namespace pa

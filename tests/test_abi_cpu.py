@@ -114,3 +114,27 @@ def test_reshape_and_cache_status_codes():
 def test_prefill_and_workspace_queries_reject_null_desc():
     assert L._lib.pa_prefill_workspace_bytes(None, 1, 1, 1, 1) == 0
     assert L._lib.pa_decode_workspace_bytes(None, 1, 1) == 0
+
+
+def prefill(desc, out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, bt_stride=32, seq_lens=FAKE, qsl=FAKE, num_seqs=3,
+            total_q=50, max_q=40, max_s=300, scale=0.1, ws=None, ws_bytes=0):
+    d = desc.c() if desc is not None else None
+    return L._lib.pa_prefill_chunk(out, q, k, v, bt, bt_stride, seq_lens, qsl, num_seqs, total_q, max_q, max_s, scale,
+                                   ctypes.byref(d) if d is not None else None, ws, ws_bytes, None)
+
+
+def test_prefill_status_codes():
+    E = L
+    assert prefill(None) == E.PA_ERR_NULL_POINTER
+    assert prefill(good_desc(), num_seqs=0) == E.PA_OK
+    assert prefill(good_desc(), total_q=0) == E.PA_OK
+    assert prefill(good_desc(), total_q=-1) == E.PA_ERR_INVALID_ARGUMENT
+    assert prefill(good_desc(), qsl=None) == E.PA_ERR_NULL_POINTER
+    assert prefill(good_desc(), scale=-1.0) == E.PA_ERR_INVALID_ARGUMENT
+    assert prefill(good_desc(qk_dim=64, v_dim=64, k_cache_bytes=64 * 16 * 1024, v_cache_bytes=64 * 16 * 1024)) \
+        in (E.PA_ERR_UNSUPPORTED, E.PA_ERR_INVALID_ARGUMENT)
+    assert prefill(good_desc(kv_format=L.PA_KV_MLA656_E4M3)) == E.PA_ERR_UNSUPPORTED
+    assert prefill(good_desc(), qsl=FAKE + 2) == E.PA_ERR_MISALIGNED
+    need = pa.pa_prefill_workspace_bytes(good_desc(), 3, 50, 40, 2000)
+    assert need == pa.pa_decode_workspace_bytes(good_desc(), 3, 2000) > 0
+    assert prefill(good_desc(), max_s=2000) == E.PA_ERR_WORKSPACE

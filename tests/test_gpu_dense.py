@@ -86,6 +86,10 @@ SHAPES = [
     ("f16", 4, 4, 128, 16, [0, 3000, 5, 1024, 1025], 1024),
     ("bf16", 4, 1, 128, 16, [1, 1000], 0),
     ("f16", 8, 1, 128, 256, [255, 256, 257, 3000], 0),
+    # few tokens per row: the softmax weights are not averaged out, so their rounding shows
+    ("bf16", 32, 8, 128, 16, [2, 3, 4, 5, 6, 7, 8, 9], 0),
+    ("bf16", 8, 8, 128, 16, [2, 3, 4, 5], 0),
+    ("bf16", 8, 8, 64, 16, [2, 3, 5], 0),
 ]
 
 

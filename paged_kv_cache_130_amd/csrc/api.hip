@@ -43,6 +43,7 @@ bool view_aligned(const pa_cache_view& v, int32_t layer, int64_t a) {
 
 constexpr int32_t kMaxBlockSize = 256;
 constexpr int32_t kDefaultPartition = 512;
+constexpr int32_t kDefaultMlaPartition = 2048;
 
 // Block sizes are powers of two from 16 to 256, so that token -> (block, row) is a shift and a mask.
 bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= kMaxBlockSize && (bs & (bs - 1)) == 0; }
@@ -56,7 +57,9 @@ int32_t log2_int(int32_t v) {
 // Tokens per split-context partition. A requested size is a multiple of block_size; partitions are
 // capped at 64 blocks, because a partition's block ids are held one per lane of a wave.
 int32_t effective_partition(const pa_attn_desc& d) {
-    int32_t P = d.partition_size > 0 ? d.partition_size : kDefaultPartition;
+    // MLA partials are 128 heads x 512 fp32 per partition, so MLA partitions default to more tokens.
+    const int32_t dflt = d.kv_format == PA_KV_MLA656_E4M3 ? kDefaultMlaPartition : kDefaultPartition;
+    int32_t P = d.partition_size > 0 ? d.partition_size : dflt;
     if (P < d.block_size) P = d.block_size;
     P -= P % d.block_size;
     const int32_t cap = 64 * d.block_size;
@@ -84,6 +87,22 @@ int32_t check_dense_desc(const pa_attn_desc& d) {
     if (st != PA_OK) return st;
     if (!view_aligned(d.k_view, d.layer, 16) || !view_aligned(d.v_view, d.layer, 16)) return PA_ERR_MISALIGNED;
     if (d.num_blocks > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;  // block ids are int32
+    return PA_OK;
+}
+
+constexpr int32_t kMlaRowBytes = 656;  // 512 e4m3 latent + 4 float32 scales + 64 bf16 RoPE
+
+int32_t check_mla_desc(const pa_attn_desc& d) {
+    if (d.num_kv_heads != 1 || d.qk_dim != 576 || d.v_dim != 512) return PA_ERR_INVALID_ARGUMENT;
+    if (d.num_q_heads <= 0 || d.num_q_heads % 16 != 0) return PA_ERR_UNSUPPORTED;
+    if (!block_size_ok(d.block_size)) return PA_ERR_UNSUPPORTED;
+    if (d.partition_size < 0 || (d.partition_size > 0 && d.partition_size % d.block_size != 0))
+        return PA_ERR_INVALID_ARGUMENT;
+    if (d.k_view.row_bytes != kMlaRowBytes) return PA_ERR_INVALID_ARGUMENT;
+    const int32_t st = check_view(d.k_view, d.layer, d.num_blocks, d.block_size, d.k_cache_bytes);
+    if (st != PA_OK) return st;
+    if (!view_aligned(d.k_view, d.layer, 16)) return PA_ERR_MISALIGNED;
+    if (d.num_blocks > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
 
@@ -161,7 +180,7 @@ int32_t pa_reshape_and_cache(const void* k, int64_t k_pitch, const void* v, int6
 
 size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t max_context_len) {
     if (!desc || num_seqs <= 0 || max_context_len <= 0) return 0;
-    if (desc->kv_format == PA_KV_F16 || desc->kv_format == PA_KV_BF16) {
+    if (desc->kv_format == PA_KV_F16 || desc->kv_format == PA_KV_BF16 || desc->kv_format == PA_KV_MLA656_E4M3) {
         if (!block_size_ok(desc->block_size)) return 0;
         return dense_decode_ws(*desc, num_seqs, max_context_len);
     }
@@ -177,11 +196,11 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
     if (!out || !q || !k_cache || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
     if (bt_stride <= 0 || !std::isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARGUMENT;
     const pa_attn_desc& d = *desc;
-    if (d.kv_format == PA_KV_MLA656_E4M3) return PA_ERR_UNSUPPORTED;
-    int32_t st = check_dense_desc(d);
+    const bool mla = d.kv_format == PA_KV_MLA656_E4M3;
+    int32_t st = mla ? check_mla_desc(d) : check_dense_desc(d);
     if (st != PA_OK) return st;
-    if (!v_cache) return PA_ERR_NULL_POINTER;
-    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+    if (!mla && !v_cache) return PA_ERR_NULL_POINTER;
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || (!mla && !aligned(v_cache, 16)) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return PA_ERR_MISALIGNED;
     const int32_t P = effective_partition(d);
@@ -197,30 +216,31 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
     p.out = out;
     p.q = q;
     p.k = static_cast<const char*>(k_cache) + d.k_view.offset + (int64_t)d.layer * d.k_view.layer_stride;
-    p.v = static_cast<const char*>(v_cache) + d.v_view.offset + (int64_t)d.layer * d.v_view.layer_stride;
+    p.v = mla ? p.k : static_cast<const char*>(v_cache) + d.v_view.offset + (int64_t)d.layer * d.v_view.layer_stride;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     const int64_t n = (int64_t)num_seqs * d.num_q_heads * max_parts;
     p.part_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
     p.part_acc = need > 0 ? static_cast<float*>(workspace) + 2 * n : nullptr;
     p.k_block_stride = d.k_view.block_stride;
-    p.v_block_stride = d.v_view.block_stride;
+    p.v_block_stride = mla ? d.k_view.block_stride : d.v_view.block_stride;
     p.num_blocks = d.num_blocks;
     p.k_row_bytes = d.k_view.row_bytes;
-    p.v_row_bytes = d.v_view.row_bytes;
+    p.v_row_bytes = mla ? d.k_view.row_bytes : d.v_view.row_bytes;
     p.bt_stride = bt_stride;
     p.num_seqs = num_seqs;
     p.num_q_heads = d.num_q_heads;
-    p.num_kv_heads = d.num_kv_heads;
+    p.num_kv_heads = mla ? d.num_q_heads / 16 : d.num_kv_heads;
     p.block_size = d.block_size;
     p.tiles_per_block_log2 = log2_int(d.block_size / 16);
     p.partition_tokens = P;
     p.max_parts = max_parts;
     p.max_context_len = max_context_len;
     p.scale_log2 = scale * 1.4426950408889634f;
-    p.is_bf16 = d.kv_format == PA_KV_BF16;
-    p.head_dim = d.qk_dim;
-    p.group = d.num_q_heads / d.num_kv_heads;
+    p.is_bf16 = d.kv_format != PA_KV_F16;
+    p.head_dim = d.v_dim;
+    p.group = mla ? 16 : d.num_q_heads / d.num_kv_heads;
+    if (mla) return hip_status(pa::launch_decode_mla(p, static_cast<hipStream_t>(stream)));
     return hip_status(pa::launch_decode_dense(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -338,9 +338,12 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DenseDecodeParams p)
         out[0] = (uint16_t)(pack2<BF16>(a[0] * inv, 0.f) & 0xFFFFu);
     } else if constexpr (DPL == 2) {
         *reinterpret_cast<uint32_t*>(out) = pack2<BF16>(a[0] * inv, a[1] * inv);
-    } else {
+    } else if constexpr (DPL == 4) {
         *reinterpret_cast<uint2*>(out) = make_uint2(pack2<BF16>(a[0] * inv, a[1] * inv),
                                                     pack2<BF16>(a[2] * inv, a[3] * inv));
+    } else {
+        *reinterpret_cast<uint4*>(out) = make_uint4(pack2<BF16>(a[0] * inv, a[1] * inv), pack2<BF16>(a[2] * inv, a[3] * inv),
+                                                    pack2<BF16>(a[4] * inv, a[5] * inv), pack2<BF16>(a[6] * inv, a[7] * inv));
     }
 }
 
@@ -385,6 +388,7 @@ hipError_t launch_decode_reduce(const DenseDecodeParams& p, hipStream_t stream) 
         switch (p.head_dim) {
             case 64: hipLaunchKernelGGL((decode_reduce_kernel<true, 64>), dim3((unsigned)red), dim3(256), 0, stream, p); break;
             case 128: hipLaunchKernelGGL((decode_reduce_kernel<true, 128>), dim3((unsigned)red), dim3(256), 0, stream, p); break;
+            case 512: hipLaunchKernelGGL((decode_reduce_kernel<true, 512>), dim3((unsigned)red), dim3(256), 0, stream, p); break;
             default: hipLaunchKernelGGL((decode_reduce_kernel<true, 256>), dim3((unsigned)red), dim3(256), 0, stream, p); break;
         }
     } else {

@@ -60,6 +60,10 @@ struct DenseDecodeParams {
 hipError_t launch_decode_dense(const DenseDecodeParams& p, hipStream_t stream);   // picks the kernel below
 hipError_t launch_decode_mfma(const DenseDecodeParams& p, hipStream_t stream);    // head_dim 128, group 2..16
 hipError_t launch_decode_reduce(const DenseDecodeParams& p, hipStream_t stream);  // partition merge
+// MLA latent decode over 656-byte rows. Same parameter block, read as: k = the MLA view's base,
+// k_row_bytes = 656, num_kv_heads = number of 16-head query groups, head_dim = 512 (value dims),
+// group = 16, is_bf16 = 1.
+hipError_t launch_decode_mla(const DenseDecodeParams& p, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Causal chunks over paged context (query length >= 2), head_dim 128, group 1..16

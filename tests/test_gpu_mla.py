@@ -1,0 +1,115 @@
+"""GPU parity of the DSA dual cache and MLA decode.
+
+The block-outer (BLHNC) allocation holds MLA L0 | MLA L1 | IDX L0 | IDX L1 per block. Both views of
+both layers are written by pa_reshape_and_cache from one slot_mapping and compared with the oracle's
+byte image. Bytes never written stay 0xFF, which decodes to NaN in e4m3, bf16 and float32, so a stray
+read shows as a non-finite output. Then MLA decode runs per layer against the oracle, within 3e-2.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_130_amd as pa
+import workloads
+from oracle import attention as A
+from oracle import cache_write as W
+from oracle import paging as P
+from helpers import MLA_ATOL, MLA_RTOL, assert_close, bits_np, dev, image_of
+
+pytestmark = pytest.mark.gpu
+
+BS = 64
+
+
+def views():
+    v, block = P.block_outer_views([("mla", 656, 2), ("indexer", 132, 2)], BS)
+    return v["mla"], v["indexer"], block
+
+
+def to_pa(view):
+    return pa.CacheView(view.offset, view.layer_stride, view.block_stride, view.row_bytes)
+
+
+def populate(case, with_oracle=True):
+    """Write every token of every layer through pa_reshape_and_cache (populate call + step call)."""
+    mla_v, idx_v, block = views()
+    img = torch.full((case.num_blocks, block), 0xFF, dtype=torch.uint8, device="cuda")
+    host = np.full(case.num_blocks * block, 0xFF, dtype=np.uint8) if with_oracle else None
+    for layer in range(case.num_layers):
+        for slots, mla_rows, idx_rows in ((case.populate_slots, case.mla_rows[layer], case.idx_rows[layer]),
+                                          (case.step_slots, case.step_mla_rows[layer], case.step_idx_rows[layer])):
+            if len(slots) == 0:
+                continue
+            pa.pa_reshape_and_cache(dev(mla_rows), dev(slots), img, to_pa(mla_v), layer, BS, case.num_blocks,
+                                    v=dev(idx_rows), v_cache=img, v_view=to_pa(idx_v))
+            if with_oracle:
+                host = W.reshape_and_cache(host, mla_rows.cpu().numpy(), slots, mla_v, layer, BS)
+                host = W.reshape_and_cache(host, idx_rows.cpu().numpy(), slots, idx_v, layer, BS)
+    torch.cuda.synchronize()
+    return img, host
+
+
+def mla_desc(case, img, layer, partition_size=0):
+    mla_v, _, _ = views()
+    return pa.AttnDesc(kv_format=pa.PA_KV_MLA656_E4M3, num_q_heads=case.num_q_heads, num_kv_heads=1, qk_dim=576,
+                       v_dim=512, block_size=BS, num_blocks=case.num_blocks, k_view=to_pa(mla_v),
+                       k_cache_bytes=img.numel(), layer=layer, partition_size=partition_size)
+
+
+def mla_decode_gpu(case, img, layer, partition_size=0):
+    desc = mla_desc(case, img, layer, partition_size)
+    B = len(case.context_lens)
+    max_ctx = int(case.context_lens.max())
+    ws = torch.empty(max(16, pa.pa_decode_workspace_bytes(desc, B, max_ctx)), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, case.num_q_heads, 512, dtype=torch.int16, device="cuda")
+    pa.pa_decode(out, dev(case.q), img, None, dev(case.block_tables), dev(case.context_lens), max_ctx, case.scale,
+                 desc, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("partition_size", [0, 64, 128, 256])
+def test_dual_cache_write_and_mla_decode_small(partition_size):
+    ctx = [1, 5, 63, 64, 65, 300, 1000, 17]
+    need = sum(P.blocks_needed(n, BS) for n in ctx)
+    case = workloads.make_mla_case(seed=900, context_lens=ctx, num_blocks=need + 3, num_q_heads=32)
+    img, host = populate(case)
+    assert np.array_equal(image_of(img), host), "dual-cache bytes differ from the oracle's reshape_and_cache"
+    mla_v, _, _ = views()
+    for layer in range(2):
+        out = mla_decode_gpu(case, img, layer, partition_size)
+        ref = A.mla_decode(bits_np(case.q), host, mla_v, layer, case.block_tables, case.context_lens, BS,
+                           case.scale)
+        got = out.view(torch.bfloat16).double().cpu().numpy()
+        assert_close(got, ref, MLA_ATOL, MLA_RTOL, f"mla layer {layer} P={partition_size}")
+
+
+def test_full_size_dsa_mla_sampled():
+    """64 seqs, ctx U[1024, 8192], 128 heads on one latent head, 2 layers, 9216 blocks x 100864 B."""
+    case = workloads.make_mla_case(device="cuda")
+    img, _ = populate(case, with_oracle=False)
+    mla_v, idx_v, block = views()
+    # Spot-check the write of a few tokens against the page's address rule.
+    for t in (0, len(case.populate_slots) // 2, len(case.populate_slots) - 1):
+        b, pos = P.split_slot(int(case.populate_slots[t]), BS)
+        for layer in range(2):
+            a = P.address(mla_v, layer, b, pos)
+            got = img.view(-1)[a:a + 656].cpu().numpy()
+            assert np.array_equal(got, case.mla_rows[layer][t].cpu().numpy())
+            a = P.address(idx_v, layer, b, pos)
+            assert np.array_equal(img.view(-1)[a:a + 132].cpu().numpy(), case.idx_rows[layer][t].cpu().numpy())
+    q = bits_np(case.q)
+    rng = np.random.default_rng(5)
+    seqs = sorted(set(rng.choice(64, size=5, replace=False).tolist()) | {int(np.argmax(case.context_lens))})
+    for layer in range(2):
+        out = mla_decode_gpu(case, img, layer)
+        got = out.view(torch.bfloat16).double().cpu().numpy()
+        assert np.isfinite(got).all()
+        for s in seqs:
+            n = int(case.context_lens[s])
+            nblk = P.blocks_needed(n, BS)
+            ids = torch.as_tensor(case.block_tables[s, :nblk].astype(np.int64), device="cuda")
+            sub = image_of(img.index_select(0, ids))
+            ref = A.mla_decode(q[s:s + 1], sub, mla_v, layer, np.arange(nblk)[None, :], [n], BS, case.scale)
+            assert_close(got[s], ref[0], MLA_ATOL, MLA_RTOL, f"layer {layer} seq {s} (ctx {n})")

@@ -1,16 +1,18 @@
 """Benchmark of the paged-KV-cache hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mha13b|gqa_prefix|gqa_prefix_copied|long_decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra] [--no-cpu-baseline]
 
-One step = one pass of the decode hot path over one batch: pa_reshape_and_cache writes each
-sequence's new K/V row through slot_mapping, then pa_decode attends every sequence to its whole
-paged context. Inputs are seeded synthetic draws already resident in HBM when timing starts.
+The JSON line is for the 13B-shaped MHA decode (64 sequences, contexts U[128, 2048], 40 heads of
+128, fp16, block size 16). One step writes each sequence's new K/V row through slot_mapping
+(pa_reshape_and_cache), then attends every sequence to its whole paged context (pa_decode). Inputs are
+seeded synthetic draws resident in HBM when timing starts.
 
-The JSON line reports the whole step's algorithmic bytes per second as `value`, with decode tokens/s
-beside it. `roofline` covers the pa_decode call (the dominant kernel): its algorithmic bytes divided
-by its own duration, from HIP events recorded on the launch stream around every call in the timed
-region. `cpu_baseline` times the NumPy oracle on the host cores over a bounded sample of the same
-batch.
+`value` is the step's algorithmic bytes per second; decode tokens/s sits beside it. `roofline` covers
+the pa_decode call (the dominant kernel): its algorithmic bytes over its own duration, from HIP events
+recorded around every call on the launch stream. `cpu_baseline` times the NumPy oracle on the host
+cores over a bounded sample of the same batch. `extra` holds short runs of the other workloads, each
+measured the same way: GQA-8 with a shared or copied 2000-token prompt, long-context decode,
+the mixed chunked-prefill steps, and the DSA dual-cache write plus MLA decode.
 """
 
 from __future__ import annotations
@@ -25,13 +27,16 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TF = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = ("api.hip", "cache_write.hip", "decode_dense.hip", "decode_mfma.hip", "decode_mla.hip",
+                  "prefill_mfma.hip", "decode_common.h", "mfma_common.h", "pa_device.h", "pa_internal.h")
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("decode_dense.hip", "decode_mfma.hip", "decode_common.h", "pa_device.h", "pa_internal.h", "api.hip"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "paged_kv_cache_130_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -43,53 +48,276 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mha13b",
-                    choices=["mha13b", "gqa_prefix", "gqa_prefix_copied", "long_decode"])
+                    choices=["mha13b", "gqa_prefix", "gqa_prefix_copied", "long_decode", "long_mixed", "dsa_mla"])
     ap.add_argument("--partition", type=int, default=0, help="pa_decode partition_size (0: library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the short runs of the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
 
 
-def build_workload(name: str):
+class Timer:
+    """HIP event pairs recorded around calls on the launch stream."""
+
+    def __init__(self, torch, n):
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.ev]
+
+
+def traffic_for(name):
+    """HBM bytes per call from the committed counter runs, if they were taken on the current kernels."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        cnt = json.load(f)
+    e = cnt.get(name)
+    if e and e.get("kernel_hash") == kernel_source_hash():
+        return e.get("hbm_bytes_per_call")
+    return None
+
+
+# --------------------------------------------------------------------------
+# Dense decode workloads
+# --------------------------------------------------------------------------
+
+def dense_case(name):
     import workloads
     if name == "mha13b":
-        case = workloads.make_dense_case("mha13b", device="cuda")
-        desc_name = "13B-shaped MHA decode: 64 seqs, ctx U[128,2048], 40/40 heads x 128, fp16, bs 16, 12288 blocks"
-    elif name in ("gqa_prefix", "gqa_prefix_copied"):
-        case = workloads.make_dense_case("gqa_prefix", device="cuda", copied_prefix=name.endswith("copied"))
-        desc_name = ("GQA decode, 256 seqs sharing a 2000-token prompt (125 blocks) + lognormal suffix, 32/8 heads x "
-                     "128, bf16, bs 16" + (", prompt blocks copied per sequence" if name.endswith("copied") else ""))
-    else:
-        case = workloads.make_dense_case("tiny", seed=1304, context_lens=[32768] * 8, num_blocks=17408,
-                                         num_q_heads=32, num_kv_heads=8, dtype="bf16", device="cuda")
-        desc_name = "long-context decode: 8 seqs x 32768 tokens, 32/8 heads x 128, bf16, bs 16, partitions of 512"
-    return case, desc_name
+        return workloads.make_dense_case("mha13b", device="cuda"), (
+            "13B-shaped MHA decode: 64 seqs, ctx U[128,2048], 40/40 heads x 128, fp16, bs 16, 12288 blocks")
+    if name in ("gqa_prefix", "gqa_prefix_copied"):
+        copied = name.endswith("copied")
+        return workloads.make_dense_case("gqa_prefix", device="cuda", copied_prefix=copied), (
+            "GQA-8 decode: 256 seqs, shared 2000-token prompt (125 blocks) + lognormal suffix (median 300), "
+            "32/8 heads x 128, bf16, bs 16" + ("; prompt blocks copied per sequence" if copied else ""))
+    return workloads.make_dense_case("tiny", seed=1304, context_lens=[32768] * 8, num_blocks=17408, num_q_heads=32,
+                                     num_kv_heads=8, dtype="bf16", device="cuda"), (
+        "long-context decode: 8 seqs x 32768 tokens, 32/8 heads x 128, bf16, bs 16, partitions of 512")
 
 
-def algorithmic_bytes(case):
-    """Bytes the method must move (distinct rows read once), for the decode call and for the cache write."""
+def dense_bytes(case):
+    """Algorithmic bytes: distinct K/V rows read once, Q, output, table entries, lengths; and the step's write."""
     import numpy as np
     ctx = case.context_lens.astype(np.int64)
     row = case.row_bytes
-    head_bytes = case.head_dim * 2
     B, Hq = case.num_seqs, case.num_q_heads
-    # distinct (block, position) rows touched: shared prompt blocks count once
     if case.extra.get("shared_prefix_blocks") and not case.extra.get("copied_prefix"):
-        shared_tokens = case.extra["shared_prefix_blocks"] * case.block_size
-        unique_tokens = int(ctx.sum() - (B - 1) * shared_tokens)
+        unique_tokens = int(ctx.sum() - (B - 1) * case.extra["shared_prefix_blocks"] * case.block_size)
     else:
         unique_tokens = int(ctx.sum())
-    nblk = int(((ctx + case.block_size - 1) // case.block_size).sum())   # block-table entries read
-    fixed = B * Hq * head_bytes * 2 + nblk * 4 + B * 4            # q + out + block-table entries + lengths
-    decode_logical = int(ctx.sum()) * 2 * row + fixed
-    decode_unique = unique_tokens * 2 * row + fixed
-    write = B * (2 * row) * 2 + B * 8                              # read + write of K and V rows, slots
-    return decode_logical, decode_unique, write
+    nblk = int(((ctx + case.block_size - 1) // case.block_size).sum())
+    fixed = B * Hq * case.head_dim * 2 * 2 + nblk * 4 + B * 4
+    return int(ctx.sum()) * 2 * row + fixed, unique_tokens * 2 * row + fixed, B * 2 * row * 2 + B * 8
 
+
+def run_dense(name, steps, warmup, partition):
+    import numpy as np
+    import torch
+    import paged_kv_cache_130_amd as pa
+    case, wdesc = dense_case(name)
+    B, Hq, D = case.num_seqs, case.num_q_heads, case.head_dim
+    kd, vd = case.k_pool, case.v_pool
+    view = pa.dense_view(case.block_size, case.num_kv_heads, D)
+    part = partition or (512 if name == "long_decode" else 0)
+    desc = pa.dense_desc(case.dtype, Hq, case.num_kv_heads, D, case.block_size, case.num_blocks, kd.numel() * 2,
+                         vd.numel() * 2, part)
+    max_ctx = int(case.context_lens.max())
+    ws = torch.empty(max(16, pa.pa_decode_workspace_bytes(desc, B, max_ctx)), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, D, dtype=torch.int16, device="cuda")
+    tables = torch.from_numpy(case.block_tables).cuda()
+    lens = torch.from_numpy(case.context_lens).cuda()
+    slots = torch.from_numpy(case.new_slots).cuda()
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        pa.pa_reshape_and_cache(case.new_k, slots, kd, view, 0, case.block_size, case.num_blocks, v=case.new_v,
+                                v_cache=vd, v_view=view)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_decode(out, case.q, kd, vd, tables, lens, max_ctx, case.scale, desc, ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    tm = Timer(torch, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(tm.ev[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    dec = tm.ms()
+    dec_mean = float(np.mean(dec))
+    logical, unique, write = dense_bytes(case)
+    achieved = unique / (dec_mean / 1e3) / 1e9
+    kernel = "decode_mfma_kernel" if (D == 128 and Hq // case.num_kv_heads >= 2) else "decode_dense_kernel"
+    return case, {
+        "workload": wdesc,
+        "ms_per_step": ms_step,
+        "value": (unique + write) / (ms_step / 1e3) / 1e9,
+        "decode_tokens_per_s": B / (ms_step / 1e3),
+        "decode_call_ms": dec_mean,
+        "decode_call_ms_p10_p90": [float(np.percentile(dec, 10)), float(np.percentile(dec, 90))],
+        "decode_kv_gbs_logical": logical / (dec_mean / 1e3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(name),
+                     "kernel": f"pa_decode ({kernel} + decode_reduce_kernel)", "algorithmic_bytes_per_call": unique},
+        "dtype": case.dtype,
+        "config": {"num_seqs": B, "num_q_heads": Hq, "num_kv_heads": case.num_kv_heads, "head_dim": D,
+                   "block_size": case.block_size, "num_blocks": case.num_blocks,
+                   "sum_context_tokens": int(case.context_lens.sum()), "partition_size": part or "auto"},
+    }
+
+
+# --------------------------------------------------------------------------
+# Mixed chunked prefill + decodes
+# --------------------------------------------------------------------------
+
+def chunk_flops(case):
+    """2 * 2 * D * (visible tokens) summed over the chunk rows and query heads (QK and PV)."""
+    total = 0
+    for s in range(len(case.seq_lens)):
+        n, ql = int(case.seq_lens[s]), int(case.query_lens[s])
+        if ql < 2:
+            continue
+        first = n - ql
+        total += sum(first + i + 1 for i in range(ql))
+    return 4 * case.head_dim * case.num_q_heads * total
+
+
+def run_mixed(steps, warmup):
+    import numpy as np
+    import torch
+    import paged_kv_cache_130_amd as pa
+    import workloads
+    res = {}
+    for st in (1, 2):
+        case = workloads.make_chunk_case(step=st, device="cuda")
+        desc = pa.dense_desc("bf16", case.num_q_heads, case.num_kv_heads, 128, 16, case.num_blocks,
+                             case.k_pool.numel() * 2, case.v_pool.numel() * 2, 512)
+        S = len(case.seq_lens)
+        max_q, max_s = int(case.query_lens.max()), int(case.seq_lens.max())
+        ws = torch.empty(max(16, pa.pa_prefill_workspace_bytes(desc, S, case.total_q, max_q, max_s)),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty(case.total_q, case.num_q_heads, 128, dtype=torch.int16, device="cuda")
+        args = [out, case.q, case.k_pool, case.v_pool, torch.from_numpy(case.block_tables).cuda(),
+                torch.from_numpy(case.seq_lens).cuda(), torch.from_numpy(case.query_start_loc).cuda(), max_q, max_s,
+                case.scale, desc, ws]
+        for _ in range(warmup):
+            pa.pa_prefill_chunk(*args)
+        tm = Timer(torch, steps)
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        for i in range(steps):
+            tm.ev[i][0].record(stream)
+            pa.pa_prefill_chunk(*args)
+            tm.ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean(tm.ms()))
+        dec_tokens = int(sum(int(n) for n, q in zip(case.seq_lens, case.query_lens) if q == 1))
+        row = case.num_kv_heads * case.head_dim * 2
+        kv_bytes = (dec_tokens + int(case.seq_lens[-1])) * 2 * row
+        fl = chunk_flops(case)
+        res[f"step{st}"] = {"chunk_tokens": int(case.query_lens[-1]), "call_ms": ms,
+                            "decode_rows_kv_bytes": dec_tokens * 2 * row, "chunk_gflop": fl / 1e9,
+                            "kv_gbs_whole_call": kv_bytes / (ms / 1e3) / 1e9,
+                            "chunk_tflops_whole_call": fl / (ms / 1e3) / 1e12}
+        del case
+    res["workload"] = ("long-context mixed call: 8 decodes at 32768 (+1 in step 2), decodes A (1000) and B (2000), "
+                       "and a 3000-token prompt chunked 2048 + 952, 32/8 heads x 128, bf16, bs 16")
+    return res
+
+
+# --------------------------------------------------------------------------
+# DSA dual cache: write through two views, then MLA decode per layer
+# --------------------------------------------------------------------------
+
+def run_mla(steps, warmup):
+    import numpy as np
+    import torch
+    import paged_kv_cache_130_amd as pa
+    import workloads
+    case = workloads.make_mla_case(device="cuda")
+    bs = case.block_size
+    page_mla, page_idx = bs * 656, bs * 132
+    mla_v = pa.CacheView(0, page_mla, case.block_bytes, 656)
+    idx_v = pa.CacheView(2 * page_mla, page_idx, case.block_bytes, 132)
+    img = torch.full((case.num_blocks, case.block_bytes), 0xFF, dtype=torch.uint8, device="cuda")
+    pop_slots = torch.from_numpy(case.populate_slots).cuda()
+    step_slots = torch.from_numpy(case.step_slots).cuda()
+    stream = torch.cuda.current_stream()
+
+    pop_ms = []  # populate each layer's two views (timed once per layer)
+    for layer in range(2):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        pa.pa_reshape_and_cache(case.mla_rows[layer], pop_slots, img, mla_v, layer, bs, case.num_blocks,
+                                v=case.idx_rows[layer], v_cache=img, v_view=idx_v)
+        b.record(stream)
+        torch.cuda.synchronize()
+        pop_ms.append(a.elapsed_time(b))
+    ntok = len(case.populate_slots)
+    B = len(case.context_lens)
+    max_ctx = int(case.context_lens.max())
+    descs = [pa.AttnDesc(kv_format=pa.PA_KV_MLA656_E4M3, num_q_heads=128, num_kv_heads=1, qk_dim=576, v_dim=512,
+                         block_size=bs, num_blocks=case.num_blocks, k_view=mla_v, k_cache_bytes=img.numel(),
+                         layer=layer) for layer in range(2)]
+    ws = torch.empty(max(16, pa.pa_decode_workspace_bytes(descs[0], B, max_ctx)), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, 128, 512, dtype=torch.int16, device="cuda")
+    tables = torch.from_numpy(case.block_tables).cuda()
+    lens = torch.from_numpy(case.context_lens).cuda()
+
+    def step(tm=None, i=0):
+        for layer in range(2):
+            pa.pa_reshape_and_cache(case.step_mla_rows[layer], step_slots, img, mla_v, layer, bs, case.num_blocks,
+                                    v=case.step_idx_rows[layer], v_cache=img, v_view=idx_v)
+            if tm is not None:
+                tm[layer].ev[i][0].record(stream)
+            pa.pa_decode(out, case.q, img, None, tables, lens, max_ctx, case.scale, descs[layer], ws)
+            if tm is not None:
+                tm[layer].ev[i][1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    tms = [Timer(torch, steps), Timer(torch, steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(tms, i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    dec_ms = float(np.mean(tms[0].ms() + tms[1].ms()))
+    sum_ctx = int(case.context_lens.sum())
+    kv = sum_ctx * 656 + B * 128 * 576 * 2 + B * 128 * 512 * 2 + int(((case.context_lens + bs - 1) // bs).sum()) * 4
+    flops = sum_ctx * 128 * (576 + 512) * 2
+    tf = flops / (dec_ms / 1e3) / 1e12
+    return {
+        "workload": ("DSA dual cache, block-outer BLHNC, 2 layers, bs 64, 9216 blocks x 100864 B; MLA decode: 64 seqs, "
+                     "ctx U[1024,8192], 128 heads on one latent head, q 512+64 bf16, fp8-e4m3 latent"),
+        "populate_write_ms_per_layer": float(np.mean(pop_ms)),
+        "populate_write_gbs": ntok * 2 * (656 + 132) / (np.mean(pop_ms) / 1e3) / 1e9,
+        "ms_per_step": ms_step,
+        "mla_decode_call_ms": dec_ms,
+        "mla_hbm_gbs": kv / (dec_ms / 1e3) / 1e9,
+        "mla_hbm_frac": kv / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
+                     "frac": tf / MFMA_BF16_PEAK_TF, "traffic": traffic_for("dsa_mla"),
+                     "kernel": "pa_decode (decode_mla_kernel + decode_reduce_kernel)",
+                     "algorithmic_flops_per_call": flops, "algorithmic_bytes_per_call": kv},
+        "sum_context_tokens": sum_ctx,
+    }
+
+
+# --------------------------------------------------------------------------
+# CPU baseline (the oracle on the host cores)
+# --------------------------------------------------------------------------
 
 def cpu_baseline(case, budget_s: float = 15.0):
-    """Oracle (NumPy fp64) on the host over a bounded sample: whole sequences in order until the budget."""
+    """Oracle (NumPy fp64) over a bounded sample: whole sequences in order until the budget is spent."""
     import numpy as np
     import torch
     try:
@@ -109,17 +337,16 @@ def cpu_baseline(case, budget_s: float = 15.0):
         ids = torch.as_tensor(case.block_tables[s, :nb].astype(np.int64), device=case.k_pool.device)
         k_img = case.k_pool.index_select(0, ids).contiguous().view(torch.uint8).reshape(-1).cpu().numpy()
         v_img = case.v_pool.index_select(0, ids).contiguous().view(torch.uint8).reshape(-1).cpu().numpy()
-        tbl = np.arange(nb)[None, :]
         t0 = time.perf_counter()
-        A.paged_decode(q[s:s + 1], case.dtype, k_img, ov, v_img, ov, 0, tbl, [n], case.block_size,
+        A.paged_decode(q[s:s + 1], case.dtype, k_img, ov, v_img, ov, 0, np.arange(nb)[None, :], [n], case.block_size,
                        case.num_kv_heads, case.head_dim, case.scale)
         spent += time.perf_counter() - t0
         done_tokens += n
         seqs += 1
         if spent >= budget_s:
             break
-    gbs = done_tokens * 2 * row / spent / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(done_tokens * 2 * row / spent / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
             "sample": f"{seqs} of {case.num_seqs} sequences (all {case.num_q_heads} heads), {done_tokens} tokens, "
                       f"{spent:.1f} s of oracle time; decode tokens/s {seqs / spent:.2f}"}
 
@@ -135,99 +362,71 @@ def calibrate_copy():
     print(json.dumps({"calibration": "device copy", "bytes_read_per_dispatch": n, "bytes_written_per_dispatch": n}))
 
 
+def rounded(x):
+    if isinstance(x, float):
+        return round(x, 4)
+    if isinstance(x, dict):
+        return {k: rounded(v) for k, v in x.items()}
+    if isinstance(x, list):
+        return [rounded(v) for v in x]
+    return x
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs on a single MI355X (no multi-GPU path). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
-    import paged_kv_cache_130_amd as pa
+    import paged_kv_cache_130_amd  # noqa: F401  (fails loudly if libpa.so is missing)
 
     if args.calibrate_copy:
         calibrate_copy()
         return
-
     torch.cuda.set_device(0)
-    case, wdesc = build_workload(args.workload)
-    B, Hq, D = case.num_seqs, case.num_q_heads, case.head_dim
-    kd, vd = case.k_pool, case.v_pool
-    view = pa.dense_view(case.block_size, case.num_kv_heads, D)
-    partition = args.partition or (512 if args.workload == "long_decode" else 0)
-    desc = pa.dense_desc(case.dtype, Hq, case.num_kv_heads, D, case.block_size, case.num_blocks, kd.numel() * 2,
-                         vd.numel() * 2, partition)
-    max_ctx = int(case.context_lens.max())
-    ws = torch.empty(max(16, pa.pa_decode_workspace_bytes(desc, B, max_ctx)), dtype=torch.uint8, device="cuda")
-    out = torch.empty(B, Hq, D, dtype=torch.int16, device="cuda")
-    q = case.q
-    tables = torch.from_numpy(case.block_tables).cuda()
-    lens = torch.from_numpy(case.context_lens).cuda()
-    slots = torch.from_numpy(case.new_slots).cuda()
-    new_k, new_v = case.new_k, case.new_v
-    stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        pa.pa_reshape_and_cache(new_k, slots, kd, view, 0, case.block_size, case.num_blocks, v=new_v, v_cache=vd,
-                                v_view=view)
-        if ev is not None:
-            ev[0].record(stream)
-        pa.pa_decode(out, q, kd, vd, tables, lens, max_ctx, case.scale, desc, ws)
-        if ev is not None:
-            ev[1].record(stream)
+    metric = "paged decode effective KV GB/s (% of HBM peak) and decode tokens/s at 1 GPU"
+    res = {"metric": metric, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "data": "synthetic (seeded N(0,1) K/V/Q, seeded block tables)"}
+    if args.workload in ("mha13b", "gqa_prefix", "gqa_prefix_copied", "long_decode"):
+        case, r = run_dense(args.workload, args.steps, args.warmup, args.partition)
+        res.update({"value": r["value"], "unit": "GB/s", "ms_per_step": r["ms_per_step"], "dtype": r["dtype"],
+                    "config": dict(workload=r["workload"], **r["config"]),
+                    "decode_tokens_per_s": r["decode_tokens_per_s"], "decode_call_ms": r["decode_call_ms"],
+                    "decode_call_ms_p10_p90": r["decode_call_ms_p10_p90"],
+                    "decode_kv_gbs_logical": r["decode_kv_gbs_logical"], "roofline": r["roofline"]})
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline(case)
+        del case
+        torch.cuda.empty_cache()
+    elif args.workload == "long_mixed":
+        r = run_mixed(args.steps, args.warmup)
+        res.update({"value": r["step1"]["kv_gbs_whole_call"], "unit": "GB/s", "ms_per_step": r["step1"]["call_ms"],
+                    "dtype": "bf16", "config": {"workload": r["workload"]}, "steps_detail": r})
+    else:
+        r = run_mla(args.steps, args.warmup)
+        res.update({"value": r["mla_hbm_gbs"], "unit": "GB/s", "ms_per_step": r["ms_per_step"], "dtype": "bf16",
+                    "config": {"workload": r["workload"]}, "roofline": r["roofline"], "mla_detail": r})
 
-    for _ in range(args.warmup):
-        step()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = [a.elapsed_time(b) for a, b in events]
-    dec_ms_mean = float(np.mean(dec_ms))
-
-    logical, unique, write = algorithmic_bytes(case)
-    value = (unique + write) / (ms_step / 1e3) / 1e9
-    achieved = unique / (dec_ms_mean / 1e3) / 1e9
-    traffic = None
-    if os.path.exists(COUNTERS):
-        with open(COUNTERS) as f:
-            cnt = json.load(f)
-        e = cnt.get(args.workload)
-        if e and e.get("kernel_hash") == kernel_source_hash():
-            traffic = e.get("hbm_bytes_per_call")
-    res = {
-        "metric": "paged decode effective KV GB/s (% of HBM peak) and decode tokens/s at 1 GPU",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": case.dtype,
-        "data": "synthetic (seeded N(0,1) K/V/Q, seeded block tables)",
-        "config": {"workload": wdesc, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": case.num_kv_heads,
-                   "head_dim": D, "block_size": case.block_size, "num_blocks": case.num_blocks,
-                   "sum_context_tokens": int(case.context_lens.sum()), "partition_size": partition or "auto"},
-        "decode_tokens_per_s": round(B / (ms_step / 1e3), 1),
-        "decode_call_ms": round(dec_ms_mean, 4),
-        "decode_call_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 4),
-                                   round(float(np.percentile(dec_ms, 90)), 4)],
-        "decode_kv_gbs_logical": round(logical / (dec_ms_mean / 1e3) / 1e9, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "pa_decode (decode_dense_kernel + decode_reduce_kernel)",
-                     "algorithmic_bytes_per_call": unique},
-    }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case)
-    print(json.dumps(res), flush=True)
+    if args.workload == "mha13b" and not args.no_extra:
+        extra = {}
+        for name in ("gqa_prefix_copied", "gqa_prefix", "long_decode"):
+            case, r = run_dense(name, 10, 3, 0)
+            extra[name] = {"workload": r["workload"], "decode_call_ms": r["decode_call_ms"],
+                           "kv_gbs": r["roofline"]["achieved"], "frac_of_hbm_peak": r["roofline"]["frac"],
+                           "kv_gbs_logical": r["decode_kv_gbs_logical"], "decode_tokens_per_s": r["decode_tokens_per_s"]}
+            del case
+            torch.cuda.empty_cache()
+        extra["long_mixed"] = run_mixed(10, 3)
+        torch.cuda.empty_cache()
+        m = run_mla(10, 3)
+        extra["dsa_mla"] = {k: m[k] for k in ("workload", "populate_write_ms_per_layer", "populate_write_gbs",
+                                              "mla_decode_call_ms", "mla_hbm_gbs", "mla_hbm_frac")}
+        extra["dsa_mla"]["mfma_tflops"] = m["roofline"]["achieved"]
+        extra["dsa_mla"]["mfma_frac"] = m["roofline"]["frac"]
+        res["extra"] = extra
+    print(json.dumps(rounded(res)), flush=True)
 
 
 if __name__ == "__main__":

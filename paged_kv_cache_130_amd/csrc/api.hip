@@ -1,6 +1,8 @@
 // Host side of the C ABI in include/pa.h: argument validation, kernel selection, launch.
 // Every check runs before anything is enqueued; no call reads device memory on the host.
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -43,7 +45,6 @@ bool view_aligned(const pa_cache_view& v, int32_t layer, int64_t a) {
 
 constexpr int32_t kMaxBlockSize = 256;
 constexpr int32_t kDefaultPartition = 512;
-constexpr int32_t kDefaultMlaPartition = 2048;
 
 // Block sizes are powers of two from 16 to 256, so that token -> (block, row) is a shift and a mask.
 bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= kMaxBlockSize && (bs & (bs - 1)) == 0; }
@@ -57,9 +58,7 @@ int32_t log2_int(int32_t v) {
 // Tokens per split-context partition. A requested size is a multiple of block_size; partitions are
 // capped at 64 blocks, because a partition's block ids are held one per lane of a wave.
 int32_t effective_partition(const pa_attn_desc& d) {
-    // MLA partials are 128 heads x 512 fp32 per partition, so MLA partitions default to more tokens.
-    const int32_t dflt = d.kv_format == PA_KV_MLA656_E4M3 ? kDefaultMlaPartition : kDefaultPartition;
-    int32_t P = d.partition_size > 0 ? d.partition_size : dflt;
+    int32_t P = d.partition_size > 0 ? d.partition_size : kDefaultPartition;
     if (P < d.block_size) P = d.block_size;
     P -= P % d.block_size;
     const int32_t cap = 64 * d.block_size;
@@ -91,19 +90,68 @@ int32_t check_dense_desc(const pa_attn_desc& d) {
 }
 
 constexpr int32_t kMlaRowBytes = 656;  // 512 e4m3 latent + 4 float32 scales + 64 bf16 RoPE
+constexpr int32_t kMlaUnit = 32;       // tokens per MLA work unit
 
 int32_t check_mla_desc(const pa_attn_desc& d) {
     if (d.num_kv_heads != 1 || d.qk_dim != 576 || d.v_dim != 512) return PA_ERR_INVALID_ARGUMENT;
     if (d.num_q_heads <= 0 || d.num_q_heads % 16 != 0) return PA_ERR_UNSUPPORTED;
     if (!block_size_ok(d.block_size)) return PA_ERR_UNSUPPORTED;
-    if (d.partition_size < 0 || (d.partition_size > 0 && d.partition_size % d.block_size != 0))
-        return PA_ERR_INVALID_ARGUMENT;
+    if (d.partition_size < 0 || d.partition_size % kMlaUnit != 0) return PA_ERR_INVALID_ARGUMENT;
     if (d.k_view.row_bytes != kMlaRowBytes) return PA_ERR_INVALID_ARGUMENT;
     const int32_t st = check_view(d.k_view, d.layer, d.num_blocks, d.block_size, d.k_cache_bytes);
     if (st != PA_OK) return st;
     if (!view_aligned(d.k_view, d.layer, 16)) return PA_ERR_MISALIGNED;
     if (d.num_blocks > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
     return PA_OK;
+}
+
+// Compute units of the current device (cached per device; 1 if the query fails).
+int32_t device_cus() {
+    static std::atomic<int32_t> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1;
+    if (dev >= 0 && dev < 64) {
+        const int32_t c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 1;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// MLA work split: heads per work-group, work-groups along the unit stream, and the partial slots
+// (num_seqs + num_wgs) the workspace holds. The grid is sized from the host bound on the units
+// (num_seqs * ceil(max_context_len / 32)); the kernel computes the exact split from context_lens.
+struct MlaLayout {
+    int32_t heads_per_wg;
+    int32_t groups;
+    int32_t num_wgs;
+    int32_t units_per_wg;  // 0: balanced over num_wgs
+    int64_t slots;
+};
+
+bool mla_layout(const pa_attn_desc& d, int32_t num_seqs, int32_t max_context_len, MlaLayout& L) {
+    const int32_t hq = d.num_q_heads;
+    L.heads_per_wg = hq % 64 == 0 ? 64 : hq % 32 == 0 ? 32 : 16;
+    L.groups = hq / L.heads_per_wg;
+    const int64_t units_max = std::max<int64_t>(1, (int64_t)num_seqs * ((max_context_len + kMlaUnit - 1) / kMlaUnit));
+    int64_t wgs;
+    if (d.partition_size > 0) {
+        L.units_per_wg = d.partition_size / kMlaUnit;
+        wgs = (units_max + L.units_per_wg - 1) / L.units_per_wg;
+    } else {
+        L.units_per_wg = 0;
+        wgs = std::min<int64_t>(std::max(1, device_cus() / L.groups), units_max);
+    }
+    if (units_max + L.units_per_wg + wgs > 0x7FFFFFFFLL || L.groups > 65535) return false;
+    L.num_wgs = (int32_t)wgs;
+    L.slots = (int64_t)num_seqs + wgs;
+    return true;
+}
+
+size_t mla_decode_ws(const MlaLayout& L, int32_t num_q_heads, int32_t num_seqs) {
+    return (size_t)L.slots * num_q_heads * (512 + 2) * sizeof(float) + (size_t)num_seqs * 2 * sizeof(int32_t);
 }
 
 size_t dense_decode_ws(const pa_attn_desc& d, int32_t num_seqs, int32_t max_context_len) {
@@ -180,9 +228,15 @@ int32_t pa_reshape_and_cache(const void* k, int64_t k_pitch, const void* v, int6
 
 size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t max_context_len) {
     if (!desc || num_seqs <= 0 || max_context_len <= 0) return 0;
-    if (desc->kv_format == PA_KV_F16 || desc->kv_format == PA_KV_BF16 || desc->kv_format == PA_KV_MLA656_E4M3) {
+    if (desc->kv_format == PA_KV_F16 || desc->kv_format == PA_KV_BF16) {
         if (!block_size_ok(desc->block_size)) return 0;
         return dense_decode_ws(*desc, num_seqs, max_context_len);
+    }
+    if (desc->kv_format == PA_KV_MLA656_E4M3) {
+        if (check_mla_desc(*desc) != PA_OK) return 0;
+        MlaLayout L;
+        if (!mla_layout(*desc, num_seqs, max_context_len, L)) return 0;
+        return mla_decode_ws(L, desc->num_q_heads, num_seqs);
     }
     return 0;
 }
@@ -203,6 +257,37 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || (!mla && !aligned(v_cache, 16)) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return PA_ERR_MISALIGNED;
+    if (mla) {
+        MlaLayout L;
+        if (!mla_layout(d, num_seqs, max_context_len, L)) return PA_ERR_UNSUPPORTED;
+        const size_t need = mla_decode_ws(L, d.num_q_heads, num_seqs);
+        if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return PA_ERR_MISALIGNED;
+        pa::MlaDecodeParams p;
+        std::memset(&p, 0, sizeof(p));
+        p.out = out;
+        p.q = q;
+        p.kv = static_cast<const char*>(k_cache) + d.k_view.offset + (int64_t)d.layer * d.k_view.layer_stride;
+        p.block_tables = block_tables;
+        p.context_lens = context_lens;
+        float* ws = static_cast<float*>(workspace);
+        p.part_acc = ws;
+        p.part_ml = ws + L.slots * d.num_q_heads * 512;
+        p.seq_meta = reinterpret_cast<int32_t*>(p.part_ml + L.slots * d.num_q_heads * 2);
+        p.block_stride = d.k_view.block_stride;
+        p.num_blocks = d.num_blocks;
+        p.bt_stride = bt_stride;
+        p.num_seqs = num_seqs;
+        p.num_q_heads = d.num_q_heads;
+        p.heads_per_wg = L.heads_per_wg;
+        p.block_size = d.block_size;
+        p.block_size_log2 = log2_int(d.block_size);
+        p.max_context_len = max_context_len;
+        p.num_wgs = L.num_wgs;
+        p.units_per_wg = L.units_per_wg;
+        p.scale_log2 = scale * 1.4426950408889634f;
+        return hip_status(pa::launch_decode_mla(p, static_cast<hipStream_t>(stream)));
+    }
     const int32_t P = effective_partition(d);
     const int64_t max_parts64 = ((int64_t)max_context_len + P - 1) / P;
     const int32_t max_parts = max_parts64 < 1 ? 1 : (int32_t)max_parts64;
@@ -216,21 +301,21 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
     p.out = out;
     p.q = q;
     p.k = static_cast<const char*>(k_cache) + d.k_view.offset + (int64_t)d.layer * d.k_view.layer_stride;
-    p.v = mla ? p.k : static_cast<const char*>(v_cache) + d.v_view.offset + (int64_t)d.layer * d.v_view.layer_stride;
+    p.v = static_cast<const char*>(v_cache) + d.v_view.offset + (int64_t)d.layer * d.v_view.layer_stride;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     const int64_t n = (int64_t)num_seqs * d.num_q_heads * max_parts;
     p.part_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
     p.part_acc = need > 0 ? static_cast<float*>(workspace) + 2 * n : nullptr;
     p.k_block_stride = d.k_view.block_stride;
-    p.v_block_stride = mla ? d.k_view.block_stride : d.v_view.block_stride;
+    p.v_block_stride = d.v_view.block_stride;
     p.num_blocks = d.num_blocks;
     p.k_row_bytes = d.k_view.row_bytes;
-    p.v_row_bytes = mla ? d.k_view.row_bytes : d.v_view.row_bytes;
+    p.v_row_bytes = d.v_view.row_bytes;
     p.bt_stride = bt_stride;
     p.num_seqs = num_seqs;
     p.num_q_heads = d.num_q_heads;
-    p.num_kv_heads = mla ? d.num_q_heads / 16 : d.num_kv_heads;
+    p.num_kv_heads = d.num_kv_heads;
     p.block_size = d.block_size;
     p.tiles_per_block_log2 = log2_int(d.block_size / 16);
     p.partition_tokens = P;
@@ -239,8 +324,7 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
     p.scale_log2 = scale * 1.4426950408889634f;
     p.is_bf16 = d.kv_format != PA_KV_F16;
     p.head_dim = d.v_dim;
-    p.group = mla ? 16 : d.num_q_heads / d.num_kv_heads;
-    if (mla) return hip_status(pa::launch_decode_mla(p, static_cast<hipStream_t>(stream)));
+    p.group = d.num_q_heads / d.num_kv_heads;
     return hip_status(pa::launch_decode_dense(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -2,6 +2,8 @@
 // list of (partition, sequence) items. Included only by .hip kernel files.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -89,5 +91,68 @@ __device__ __forceinline__ bool find_work(int w, const DenseDecodeParams& p, int
     return false;
 }
 
+// Merge n >= 1 partials (m_i, l_i, acc_i) of one (sequence, head) row, computed by one wave:
+//     out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i,   M = max_i m_i
+// (m in the log2 domain; acc_i unnormalised, sharing m_i's reference). Partial i's (m, l) pair is at
+// ml + i * ml_stride and its D accumulators at acc + i * acc_stride. The weights 2^(m_i - M) / L are
+// computed once, lane i % 64 holding partial i's, and broadcast with v_readlane; the accumulators of
+// 16 partials are loaded per unrolled step so that many loads are in flight.
+template <bool BF16, int D>
+__device__ __forceinline__ void merge_partials(const float* ml, int64_t ml_stride, const float* acc,
+                                               int64_t acc_stride, int n, uint16_t* out) {
+    constexpr int DPL = D / 64;  // output values per lane
+    constexpr int U = 16;        // partials per unrolled step
+    const int lane = threadIdx.x & 63;
+    float M = kNegInf;
+    for (int i = lane; i < n; i += 64) M = fmaxf(M, ml[i * ml_stride]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.f;
+    for (int i = lane; i < n; i += 64) L += fast_exp2(ml[i * ml_stride] - M) * ml[i * ml_stride + 1];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+    const float invL = L > 0.f ? 1.f / L : 0.f;
+    float a[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) a[k] = 0.f;
+    const float* ap = acc + lane * DPL;
+    for (int base = 0; base < n; base += 64) {
+        const int i = base + lane;
+        const float wl = i < n ? fast_exp2(ml[i * ml_stride] - M) * invL : 0.f;  // 0 past the last partial
+        const int cnt = min(64, n - base);
+        // Full steps of U partials, then steps of 4; indexes past cnt - 1 load a valid duplicate
+        // whose weight is 0.
+        auto step = [&](auto width, int j0) {
+            constexpr int C = decltype(width)::value;
+            float v[C][DPL];
+#pragma unroll
+            for (int u = 0; u < C; ++u) {
+                const int jj = min(j0 + u, cnt - 1);
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) v[u][k] = ap[(base + jj) * acc_stride + k];
+            }
+#pragma unroll
+            for (int u = 0; u < C; ++u) {
+                const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j0 + u));
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) a[k] = fmaf(w, v[u][k], a[k]);
+            }
+        };
+        int j0 = 0;
+        for (; j0 + U <= cnt; j0 += U) step(std::integral_constant<int, U>{}, j0);
+        for (; j0 < cnt; j0 += 4) step(std::integral_constant<int, 4>{}, j0);
+    }
+    uint16_t* o = out + lane * DPL;
+    if constexpr (DPL == 1) {
+        o[0] = (uint16_t)(pack2<BF16>(a[0], 0.f) & 0xFFFFu);
+    } else if constexpr (DPL == 2) {
+        *reinterpret_cast<uint32_t*>(o) = pack2<BF16>(a[0], a[1]);
+    } else if constexpr (DPL == 4) {
+        *reinterpret_cast<uint2*>(o) = make_uint2(pack2<BF16>(a[0], a[1]), pack2<BF16>(a[2], a[3]));
+    } else {
+        *reinterpret_cast<uint4*>(o) = make_uint4(pack2<BF16>(a[0], a[1]), pack2<BF16>(a[2], a[3]),
+                                                  pack2<BF16>(a[4], a[5]), pack2<BF16>(a[6], a[7]));
+    }
+}
 
 }  // namespace pa

@@ -305,46 +305,16 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
 // One wave per (sequence, query head): merge the partition partials of sequences with > 1 partition.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DenseDecodeParams p) {
-    constexpr int DPL = D / 64;  // output values per lane
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
     const int item = blockIdx.x * 4 + wave;  // = s * Hq + head
     if (item >= p.num_seqs * p.num_q_heads) return;
     const int s = item / p.num_q_heads;
     const int head = item - s * p.num_q_heads;
     const int nparts = __builtin_amdgcn_readfirstlane(parts_of(s, p));
     if (nparts <= 1) return;
-    const float* ml = p.part_ml + (size_t)item * p.max_parts * 2;
-    float M = kNegInf;
-    for (int i = lane; i < nparts; i += 64) M = fmaxf(M, ml[2 * i]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float L = 0.f;
-    for (int i = lane; i < nparts; i += 64) L += fast_exp2(ml[2 * i] - M) * ml[2 * i + 1];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
-    float a[DPL];
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) a[k] = 0.f;
-    const float* ap = p.part_acc + (size_t)item * p.max_parts * D + lane * DPL;
-    for (int i = 0; i < nparts; ++i) {
-        const float w = fast_exp2(ml[2 * i] - M);
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) a[k] = fmaf(w, ap[(size_t)i * D + k], a[k]);
-    }
-    const float inv = 1.f / L;
-    uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + ((size_t)query_row(s, p) * p.num_q_heads + head) * D + lane * DPL;
-    if constexpr (DPL == 1) {
-        out[0] = (uint16_t)(pack2<BF16>(a[0] * inv, 0.f) & 0xFFFFu);
-    } else if constexpr (DPL == 2) {
-        *reinterpret_cast<uint32_t*>(out) = pack2<BF16>(a[0] * inv, a[1] * inv);
-    } else if constexpr (DPL == 4) {
-        *reinterpret_cast<uint2*>(out) = make_uint2(pack2<BF16>(a[0] * inv, a[1] * inv),
-                                                    pack2<BF16>(a[2] * inv, a[3] * inv));
-    } else {
-        *reinterpret_cast<uint4*>(out) = make_uint4(pack2<BF16>(a[0] * inv, a[1] * inv), pack2<BF16>(a[2] * inv, a[3] * inv),
-                                                    pack2<BF16>(a[4] * inv, a[5] * inv), pack2<BF16>(a[6] * inv, a[7] * inv));
-    }
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + ((size_t)query_row(s, p) * p.num_q_heads + head) * D;
+    merge_partials<BF16, D>(p.part_ml + (size_t)item * p.max_parts * 2, 2, p.part_acc + (size_t)item * p.max_parts * D,
+                            D, nparts, out);
 }
 
 namespace {

@@ -60,10 +60,40 @@ struct DenseDecodeParams {
 hipError_t launch_decode_dense(const DenseDecodeParams& p, hipStream_t stream);   // picks the kernel below
 hipError_t launch_decode_mfma(const DenseDecodeParams& p, hipStream_t stream);    // head_dim 128, group 2..16
 hipError_t launch_decode_reduce(const DenseDecodeParams& p, hipStream_t stream);  // partition merge
-// MLA latent decode over 656-byte rows. Same parameter block, read as: k = the MLA view's base,
-// k_row_bytes = 656, num_kv_heads = number of 16-head query groups, head_dim = 512 (value dims),
-// group = 16, is_bf16 = 1.
-hipError_t launch_decode_mla(const DenseDecodeParams& p, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// MLA latent decode over 656-byte rows (one latent K/V head, num_q_heads query heads)
+// ---------------------------------------------------------------------------
+// Work is counted in units of 32 consecutive tokens of one sequence. The units of all sequences,
+// in sequence order, form one stream; work-group w takes units [w * per, (w + 1) * per) of it
+// (per = units_per_wg, or ceil(total / num_wgs) when units_per_wg is 0) for heads
+// [blockIdx.y * heads_per_wg, +heads_per_wg). A run of units of one sequence inside one range is a
+// segment. A segment that is the whole sequence writes out directly; otherwise it writes a partial
+// to slot s + w, and the merge kernel combines the slots of each sequence. (s + w grows by at least
+// one from each segment to the next, so slots are distinct and below num_seqs + num_wgs.)
+struct MlaDecodeParams {
+    void* out;                 // bf16 [num_seqs, Hq, 512]
+    const void* q;             // bf16 [num_seqs, Hq, 576]
+    const char* kv;            // cache base + view offset + layer * layer_stride
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* part_ml;            // [slots, Hq, 2]: reference max (log2 domain), sum
+    float* part_acc;           // [slots, Hq, 512]: unnormalised accumulator
+    int32_t* seq_meta;         // [num_seqs, 2]: first and last work-group of the sequence
+    int64_t block_stride;
+    int64_t num_blocks;
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t heads_per_wg;      // 128, 96, 64, 32 or 16, dividing num_q_heads
+    int32_t block_size;
+    int32_t block_size_log2;
+    int32_t max_context_len;   // clamp for context_lens
+    int32_t num_wgs;           // work-groups along x
+    int32_t units_per_wg;      // 0: balanced over num_wgs
+    float scale_log2;          // softmax scale * log2(e)
+};
+hipError_t launch_decode_mla(const MlaDecodeParams& p, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Causal chunks over paged context (query length >= 2), head_dim 128, group 1..16

@@ -22,8 +22,8 @@ pytestmark = pytest.mark.gpu
 BS = 64
 
 
-def views():
-    v, block = P.block_outer_views([("mla", 656, 2), ("indexer", 132, 2)], BS)
+def views(bs=BS):
+    v, block = P.block_outer_views([("mla", 656, 2), ("indexer", 132, 2)], bs)
     return v["mla"], v["indexer"], block
 
 
@@ -33,7 +33,8 @@ def to_pa(view):
 
 def populate(case, with_oracle=True):
     """Write every token of every layer through pa_reshape_and_cache (populate call + step call)."""
-    mla_v, idx_v, block = views()
+    bs = case.block_size
+    mla_v, idx_v, block = views(bs)
     img = torch.full((case.num_blocks, block), 0xFF, dtype=torch.uint8, device="cuda")
     host = np.full(case.num_blocks * block, 0xFF, dtype=np.uint8) if with_oracle else None
     for layer in range(case.num_layers):
@@ -41,19 +42,19 @@ def populate(case, with_oracle=True):
                                           (case.step_slots, case.step_mla_rows[layer], case.step_idx_rows[layer])):
             if len(slots) == 0:
                 continue
-            pa.pa_reshape_and_cache(dev(mla_rows), dev(slots), img, to_pa(mla_v), layer, BS, case.num_blocks,
+            pa.pa_reshape_and_cache(dev(mla_rows), dev(slots), img, to_pa(mla_v), layer, bs, case.num_blocks,
                                     v=dev(idx_rows), v_cache=img, v_view=to_pa(idx_v))
             if with_oracle:
-                host = W.reshape_and_cache(host, mla_rows.cpu().numpy(), slots, mla_v, layer, BS)
-                host = W.reshape_and_cache(host, idx_rows.cpu().numpy(), slots, idx_v, layer, BS)
+                host = W.reshape_and_cache(host, mla_rows.cpu().numpy(), slots, mla_v, layer, bs)
+                host = W.reshape_and_cache(host, idx_rows.cpu().numpy(), slots, idx_v, layer, bs)
     torch.cuda.synchronize()
     return img, host
 
 
 def mla_desc(case, img, layer, partition_size=0):
-    mla_v, _, _ = views()
+    mla_v, _, _ = views(case.block_size)
     return pa.AttnDesc(kv_format=pa.PA_KV_MLA656_E4M3, num_q_heads=case.num_q_heads, num_kv_heads=1, qk_dim=576,
-                       v_dim=512, block_size=BS, num_blocks=case.num_blocks, k_view=to_pa(mla_v),
+                       v_dim=512, block_size=case.block_size, num_blocks=case.num_blocks, k_view=to_pa(mla_v),
                        k_cache_bytes=img.numel(), layer=layer, partition_size=partition_size)
 
 
@@ -83,6 +84,43 @@ def test_dual_cache_write_and_mla_decode_small(partition_size):
                            case.scale)
         got = out.view(torch.bfloat16).double().cpu().numpy()
         assert_close(got, ref, MLA_ATOL, MLA_RTOL, f"mla layer {layer} P={partition_size}")
+
+
+# heads, block size, contexts (a zero context included), work-group range in tokens (0: balanced)
+MLA_SHAPES = [
+    (16, 16, [0, 1, 15, 16, 17, 31, 33, 200], 0),
+    (16, 16, [40, 0, 129, 7], 64),
+    (64, 32, [31, 32, 33, 95, 600, 0, 2], 0),
+    (128, 128, [127, 128, 129, 1000, 3, 0], 0),
+    (128, 64, [1, 2, 3, 700, 64, 65], 32),
+    (48, 256, [255, 256, 257, 40], 96),
+]
+
+
+@pytest.mark.parametrize("hq,bs,ctx,part", MLA_SHAPES)
+def test_mla_decode_shapes(hq, bs, ctx, part):
+    need = sum(P.blocks_needed(n, bs) for n in ctx)
+    case = workloads.make_mla_case(seed=910 + hq + bs, context_lens=ctx, num_blocks=need + 2, num_q_heads=hq,
+                                   block_size=bs)
+    img, host = populate(case)
+    assert np.array_equal(image_of(img), host), "dual-cache bytes differ from the oracle's reshape_and_cache"
+    mla_v, _, _ = views(bs)
+    for layer in range(2):
+        out = mla_decode_gpu(case, img, layer, part)
+        ref = A.mla_decode(bits_np(case.q), host, mla_v, layer, case.block_tables, case.context_lens, bs, case.scale)
+        got = out.view(torch.bfloat16).double().cpu().numpy()
+        assert np.isfinite(got).all()
+        assert_close(got, ref, MLA_ATOL, MLA_RTOL, f"mla hq={hq} bs={bs} layer {layer} P={part}")
+
+
+def test_mla_decode_is_deterministic():
+    ctx = [500, 1, 70, 0, 333]
+    need = sum(P.blocks_needed(n, BS) for n in ctx)
+    case = workloads.make_mla_case(seed=977, context_lens=ctx, num_blocks=need + 1, num_q_heads=64)
+    img, _ = populate(case, with_oracle=False)
+    a = mla_decode_gpu(case, img, 1, 64)
+    b = mla_decode_gpu(case, img, 1, 64)
+    assert torch.equal(a, b)
 
 
 def test_full_size_dsa_mla_sampled():

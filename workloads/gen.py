@@ -397,11 +397,11 @@ class MlaCase:
 
 def make_mla_case(device: str = "cpu", seed: int | None = None, context_lens=None,
                   num_blocks: int | None = None, num_q_heads: int | None = None,
-                  with_rows: bool = True) -> MlaCase:
+                  with_rows: bool = True, block_size: int | None = None) -> MlaCase:
     p = workload("dsa_mla")
     seed = p["seed"] if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
-    bs = p["block_size"]
+    bs = block_size or p["block_size"]
     ctx = (np.asarray(context_lens, dtype=np.int32) if context_lens is not None
            else draw_context_lens(rng, "dsa_mla", p))
     nb = num_blocks or p["num_blocks"]

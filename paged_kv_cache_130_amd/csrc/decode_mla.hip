@@ -36,6 +36,7 @@ namespace pa {
 namespace {
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRow = 656;                          // bytes per cached token row
 constexpr int kScaleOff = 512;                     // 4 x float32
@@ -75,18 +76,36 @@ __device__ __forceinline__ char* tile_stage() {
     else return s_tile1;
 }
 
-// 16-byte chunk c of tile row r is stored at chunk c ^ swz(r). The eight rows a group of eight lanes
-// reads at once for the score operand (16t + sigma(m), m = 0..7 or 8..15) get distinct swizzles.
-// Tile rows are 1152 bytes, a multiple of the 128-byte bank cycle, so unswizzled they would collide.
-__device__ __forceinline__ int swz(int r) { return ((r & 1) << 2) | ((r >> 2) & 3); }
+// 16-byte chunk c of tile row r is stored at chunk c ^ swz(r). Tile rows are 1152 bytes, a multiple
+// of the 128-byte bank cycle, so unswizzled the rows read together would collide. With this swizzle
+// the eight rows a group of eight lanes reads for the score operand (16t + sigma(m), m = 0..7 or
+// 8..15) get eight different swizzles, and the rows g4 + 4i read for the value operand differ in
+// the swizzle's upper two bits.
+__device__ __forceinline__ int swz(int r) { return (((r >> 2) & 3) << 1) | (r & 1); }
 
 // s_waitcnt immediate: wait until at most vm vector-memory operations are outstanding and all LDS
 // operations are done (expcnt not waited on).
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | ((vm >> 4) << 14); }
 
-__device__ __forceinline__ int mla_ctx(int s, const MlaDecodeParams& p) {
+// Read of a wave-uniform address through the constant address space, so that it becomes a scalar
+// load (counted by lgkmcnt). A vector load here would be counted by vmcnt, and waiting for it would
+// also wait for every row copy issued before it. Only for data no kernel of the call writes.
+template <typename T>
+__device__ __forceinline__ T load_scalar(const T* ptr) {
+    return *(const __attribute__((address_space(4))) T*)ptr;
+}
+
+__device__ __forceinline__ int clamp_ctx(int64_t ctx, const MlaDecodeParams& p) {
     const int64_t cap = min((int64_t)p.max_context_len, (int64_t)p.bt_stride * p.block_size);
-    return (int)max((int64_t)0, min((int64_t)p.context_lens[s], cap));
+    return (int)max((int64_t)0, min(ctx, cap));
+}
+
+// Context of sequence s (per lane).
+__device__ __forceinline__ int mla_ctx(int s, const MlaDecodeParams& p) { return clamp_ctx(p.context_lens[s], p); }
+
+// Context of sequence s, s wave-uniform.
+__device__ __forceinline__ int mla_ctx_uniform(int s, const MlaDecodeParams& p) {
+    return clamp_ctx(load_scalar(p.context_lens + s), p);
 }
 
 __device__ __forceinline__ int wave_sum_int(int v) {
@@ -110,7 +129,7 @@ __device__ __forceinline__ void advance(Cursor& c, const MlaDecodeParams& p) {
     c.k = 0;
     do {
         ++c.s;
-        c.ctx = c.s < p.num_seqs ? __builtin_amdgcn_readfirstlane(mla_ctx(c.s, p)) : 0;
+        c.ctx = c.s < p.num_seqs ? mla_ctx_uniform(c.s, p) : 0;
         c.nu = (c.ctx + kUnit - 1) / kUnit;
     } while (c.nu == 0 && c.s < p.num_seqs);
 }
@@ -171,22 +190,23 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 
 }  // namespace
 
-// NT: 16-head tiles per wave; NW: waves per work-group (heads_per_wg = 16 * NT * NW).
-template <int NT, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NW: waves per work-group; each wave owns 16 heads (heads_per_wg = 16 * NW). With 8 waves (128
+// heads) two waves share each SIMD, so one wave's vector and LDS work overlaps the other's MFMAs;
+// that caps a wave at 256 registers: 128 accumulators for its 16 x 512 output, 72 for its queries.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 4 ? 2 : 1, NW > 4 ? 2 : 1)))
 void decode_mla_kernel(MlaDecodeParams p) {
     constexpr int R = (kWindows + NW - 1) / NW;  // load instructions per lane per unit
-    constexpr int kLatentIters = (kLatentChunks + 64 * NW - 1) / (64 * NW);
+    constexpr int kLatentIters = kUnit / NW;     // tile rows each wave dequantizes per unit
     constexpr int kRopeIters = (kRopeChunks + 64 * NW - 1) / (64 * NW);
+    constexpr int kDimTiles = 32;                // 512 value dims in 16-dim output tiles
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int lane = threadIdx.x & 63;
-    int c = lane & 15;
-    int g4 = lane >> 4;
     int tid = wave * 64 + lane;
     const int w = blockIdx.x;
     const int Hq = p.num_q_heads;
-    const int head0 = blockIdx.y * p.heads_per_wg + wave * 16 * NT;  // first head of this wave
+    const int head0 = blockIdx.y * p.heads_per_wg + wave * 16;  // first head of this wave
 
     const int U = total_units(p, lane);
     const int per = p.units_per_wg > 0 ? p.units_per_wg : (U + p.num_wgs - 1) / p.num_wgs;
@@ -198,20 +218,33 @@ void decode_mla_kernel(MlaDecodeParams p) {
     const uint32_t nb = (uint32_t)p.num_blocks;
     const float sl2 = p.scale_log2;
 
-    // Per-lane LDS offsets. Score operand (A = K): row 16t + sigma(c), chunk 4ks + g4, swizzled; the
-    // swizzled chunk is 8 (ks >> 1) + ((4 (ks & 1)) ^ x) with x = g4 ^ swz(row).
-    const int arow = sigma(c);
-    const int ax = g4 ^ swz(arow);
-    int a_even = arow * kTileRow + (ax << 4);
-    int a_odd = arow * kTileRow + ((ax ^ 4) << 4);
-    // PV operand (B = V): rows 16t + g4 + 4i, dims 128q + 8c .. +7 (chunk 16q + c, swizzled).
-    int vbase[4];
+    // Per-lane LDS offsets (c = lane % 16, g4 = lane / 16).
+    // Score operand (A = K): row 16t + sigma(c), chunk 4ks + g4, swizzled: the physical chunk is
+    // 8 (ks >> 1) + ((4 (ks & 1)) ^ x) with x = g4 ^ swz(row).
+    int a_even, a_odd;
+    // Value operand (B = V), read with ds_read_b64_tr_b16: in each 16-lane block (lane group g4) lane
+    // n supplies the address of 4 dims (16dt + 4 (n & 3) .. +3) of row 16t + g4 + 4 (n >> 2), and lane
+    // i receives dim 16dt + i of the four rows g4, g4 + 4, g4 + 8, g4 + 12: exactly k-slots 0..3
+    // (t = 0) or 4..7 (t = 1) of a 16x16x32 B operand whose column i is dim 16dt + i. The physical
+    // chunk of that 8-byte piece is 8 (dt >> 2) + 2 ((dt & 3) ^ j) + (h ^ (g4 & 1)) with j = n >> 2,
+    // h = (n >> 1) & 1; trbase[d3] holds everything but the dt >> 2 part, for d3 = dt & 3.
+    int trbase[4];
+    auto lane_offsets = [&]() __attribute__((always_inline)) {
+        const int c = lane & 15, g4 = lane >> 4;
+        const int arow = sigma(c);
+        const int ax = g4 ^ swz(arow);
+        a_even = arow * kTileRow + (ax << 4);
+        a_odd = arow * kTileRow + ((ax ^ 4) << 4);
+        const int j = c >> 2, h = (c >> 1) & 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vbase[i] = (g4 + 4 * i) * kTileRow + ((c ^ (((g4 & 1) << 2) | i)) << 4);
+        for (int d3 = 0; d3 < 4; ++d3)
+            trbase[d3] = (g4 + 4 * j) * kTileRow + ((2 * (d3 ^ j) + (h ^ (g4 & 1))) << 4) + ((c & 1) << 3);
+    };
+    lane_offsets();
 
-    uint4 qr[NT][kKSteps];
-    f32x4_t O[NT][4][8];  // [head tile][latent quarter q][dim 128q + 8c + e]
-    float m[NT], l[NT];
+    uint4 qr[kKSteps];
+    f32x4_t O[kDimTiles];  // register j of lane (c, g4): head 4 g4 + j, dim 16 dt + c
+    float m = kNegInf, l = 0.f;
     // Unit validity, one slot per raw stage: bits 0..7 valid rows, bit 8 / 9 rows 0..15 / 16..31 in a
     // valid block.
     int info[4];
@@ -221,75 +254,118 @@ void decode_mla_kernel(MlaDecodeParams p) {
     bool seg_from_start = false;           // the current segment began at the sequence's first unit
 
     // Empty asm statements that tie the queries to vector registers and the outputs to accumulation
-    // registers once per step. Without them the register allocator is free to move the queries (an
-    // MFMA B operand may come from either file) into the accumulation registers, which pushes the
-    // outputs out and costs hundreds of register-to-register copies per step.
+    // registers once per step. Without them the register allocator may move the queries (an MFMA B
+    // operand may come from either file) into the accumulation registers, which pushes the outputs
+    // out and costs hundreds of register-to-register copies per step.
     auto pin_outputs = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) asm volatile("" : "+a"(O[n][q][e]));
+        for (int dt = 0; dt < kDimTiles; ++dt) asm volatile("" : "+a"(O[dt]));
     };
-    auto pin_registers = [&]() __attribute__((always_inline)) {
-        asm volatile("" : "+v"(lane), "+v"(c), "+v"(g4), "+v"(tid), "+v"(a_even), "+v"(a_odd), "+v"(vbase[0]),
-                     "+v"(vbase[1]), "+v"(vbase[2]), "+v"(vbase[3]));
+    auto pin_queries = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks) {
-                u32x4 t = __builtin_bit_cast(u32x4, qr[n][ks]);
-                asm volatile("" : "+v"(t));
-                qr[n][ks] = __builtin_bit_cast(uint4, t);
-            }
-        pin_outputs();
+        for (int ks = 0; ks < kKSteps; ++ks) {
+            u32x4 t = __builtin_bit_cast(u32x4, qr[ks]);
+            asm volatile("" : "+v"(t));
+            qr[ks] = __builtin_bit_cast(uint4, t);
+        }
     };
 
-    // Copies unit cl into raw stage K, records its validity in info[K], and advances cl.
+    // Row copy. Chunk kk of a unit (41 per row) is loaded by lane kk % 64 of wave (kk / 64) % NW in
+    // round kk / (64 NW). A lane whose chunk is past the unit's valid rows reloads the last valid
+    // chunk into its own LDS slot (a row that is never read); a unit with no valid rows (past the
+    // range, or in an invalid block) reads the first 16 bytes of q instead. So every wave issues the
+    // same R loads per unit, which the vmcnt accounting relies on.
+    int dma_kk[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) dma_kk[r] = (r * NW + wave) * 64 + lane;
+
+    // Block ids of unit cl, read one step before its copy is issued so that the scalar-load latency
+    // is hidden (pre_pb: rows 16..31 when block_size is 16).
+    int pre_pa = 0, pre_pb = 0;
+    auto prefetch_ids = [&]() __attribute__((always_inline)) {
+        if (cl.g < g_end) {
+            const int t0 = cl.k * kUnit;
+            const int32_t* bt = p.block_tables + (int64_t)cl.s * p.bt_stride;
+            const int lb = t0 >> p.block_size_log2;
+            pre_pa = load_scalar(bt + lb);
+            pre_pb = (p.block_size < kUnit && cl.ctx - t0 > 16) ? load_scalar(bt + lb + 1) : pre_pa;
+        }
+    };
+
+    // Copies unit cl into raw stage K, records its validity in info[K], advances cl and prefetches the
+    // next unit's block ids.
     auto issue = [&](auto kst) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
         const bool live = cl.g < g_end;
         int v = 0;
-        int64_t off_a = 0, off_b = 0;
+        const char* base_a = dummy;              // rows 0..15 (all rows when block_size >= 32)
+        const char* base_b = dummy - 16 * kRow;  // rows 16..31, addressed by chunk kk >= 16 * 41
+        int lim_a = 0, lim_b = 16 * 41;
         bool ok_a = false, ok_b = false;
         if (live) {
             v = min(kUnit, cl.ctx - cl.k * kUnit);
             const int t0 = cl.k * kUnit;
-            const int32_t* bt = p.block_tables + (int64_t)cl.s * p.bt_stride;
-            const int lb = t0 >> p.block_size_log2;
-            const int pa = bt[lb];
+            const int pa = pre_pa;
             ok_a = (uint32_t)pa < nb;
-            off_a = (int64_t)pa * p.block_stride + (int64_t)(t0 & (p.block_size - 1)) * kRow;
-            if (p.block_size < kUnit) {  // block size 16: rows 16..31 are in the next block
-                const int pb = v > 16 ? bt[lb + 1] : pa;
-                ok_b = (uint32_t)pb < nb;
-                off_b = (int64_t)pb * p.block_stride - 16 * kRow;
-            } else {
+            if (p.block_size >= kUnit) {
                 ok_b = ok_a;
-                off_b = off_a;
+                if (ok_a) {
+                    base_a = p.kv + (int64_t)pa * p.block_stride + (int64_t)(t0 & (p.block_size - 1)) * kRow;
+                    lim_a = v * 41 - 1;
+                }
+            } else {  // block size 16: rows 16..31 are in the next block
+                if (ok_a) {
+                    base_a = p.kv + (int64_t)pa * p.block_stride;
+                    lim_a = min(v, 16) * 41 - 1;
+                }
+                if (v > 16) {
+                    const int pb = pre_pb;
+                    ok_b = (uint32_t)pb < nb;
+                    if (ok_b) {
+                        base_b = p.kv + (int64_t)pb * p.block_stride - 16 * kRow;
+                        lim_b = v * 41 - 1;
+                    }
+                }
             }
         }
         info[K] = v | (ok_a ? 0x100 : 0) | (ok_b ? 0x200 : 0);
         char* stage = raw_stage<K>();
+        const bool split = p.block_size < kUnit;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int win = r * NW + wave;
-            const int kk = win * 64 + lane;  // chunk; row kk / 41, since a row is 41 chunks
-            const int row = kk / 41;
-            const bool use = kk < v * 41 && (row < 16 ? ok_a : ok_b);
-            const char* src = use ? p.kv + (row < 16 ? off_a : off_b) + (int64_t)kk * 16 : dummy;
+            const int kk = dma_kk[r];
+            const bool hi = split && kk >= 16 * 41;
+            const char* src = (hi ? base_b : base_a) + (int64_t)min(kk, hi ? lim_b : lim_a) * 16;
             char* dst = win < kWindows ? stage + win * 1024 : s_junk;
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                              (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
         advance(cl, p);
+        prefetch_ids();
     };
 
-    // Dequantizes latent items [i0, i0 + CNT) (and, if rope, the RoPE chunks) of the unit in raw
-    // stage KR (validity vi) into tile stage KT. Branch-free: rows past the valid ones read stale LDS
-    // bytes and write zeros.
-    auto convert = [&](auto kr, auto kt, int vi, int i0, auto cnt, bool rope) __attribute__((always_inline)) {
+    // Dequantization of a unit: raw stage KR (validity vi) -> tile stage KT. Item it is row
+    // it * NW + wave (the same for the whole wave), 8 bytes per lane; rows past the valid ones write
+    // zeros (their stale LDS bytes are read but not used). conv_load issues the LDS reads of all
+    // items; conv_store converts and writes items [i0, i0 + CNT) and, if rope, the RoPE chunks.
+    struct ConvIn {
+        uint2 b8[kLatentIters];
+        float sc[kLatentIters];
+    };
+    auto conv_load = [&](auto kr, ConvIn& in) __attribute__((always_inline)) {
+        constexpr int KR = decltype(kr)::value;
+        const char* raw = raw_stage<KR>();
+        const int conv_raw = wave * kRow + 8 * lane;
+        const int conv_scale = wave * kRow + kScaleOff + 4 * (lane >> 4);
+#pragma unroll
+        for (int it = 0; it < kLatentIters; ++it) {
+            in.b8[it] = *reinterpret_cast<const uint2*>(raw + conv_raw + it * NW * kRow);
+            in.sc[it] = *reinterpret_cast<const float*>(raw + conv_scale + it * NW * kRow);
+        }
+    };
+    auto conv_store = [&](auto kr, auto kt, int vi, const ConvIn& in, int i0, auto cnt, bool rope)
+        __attribute__((always_inline)) {
         constexpr int KR = decltype(kr)::value;
         constexpr int KT = decltype(kt)::value;
         constexpr int CNT = decltype(cnt)::value;
@@ -300,14 +376,11 @@ void decode_mla_kernel(MlaDecodeParams p) {
 #pragma unroll
         for (int jj = 0; jj < CNT; ++jj) {
             const int it = i0 + jj;
-            const int n = it * 64 * NW + tid;
-            if (it < kLatentIters && (kLatentChunks % (64 * NW) == 0 || n < kLatentChunks)) {
-                const int r = n >> 6, ch = n & 63;
-                const uint2 b8 = *reinterpret_cast<const uint2*>(raw + r * kRow + 8 * ch);
-                const float sc = *reinterpret_cast<const float*>(raw + r * kRow + kScaleOff + 4 * (ch >> 4));
-                const uint4 d = dequant8(b8, sc);
+            if (it < kLatentIters) {
+                const int r = it * NW + wave;  // wave-uniform
+                const uint4 d = dequant8(in.b8[it], in.sc[it]);
                 const bool keep = r < v && (r < 16 ? ok_a : ok_b);
-                *reinterpret_cast<uint4*>(tile + r * kTileRow + ((ch ^ swz(r)) << 4)) =
+                *reinterpret_cast<uint4*>(tile + r * kTileRow + ((lane ^ swz(r)) << 4)) =
                     keep ? d : make_uint4(0u, 0u, 0u, 0u);
             }
         }
@@ -326,22 +399,28 @@ void decode_mla_kernel(MlaDecodeParams p) {
         }
     };
 
+    // Per-lane offsets pass through an empty asm statement at every step. The LDS objects span
+    // 160 KB, beyond the 64 KB immediate offset of the LDS instructions, so each (object, per-lane
+    // offset) pair would otherwise become its own long-lived register; recomputing costs one add.
+    auto refresh_offsets = [&]() __attribute__((always_inline)) {
+        asm volatile("" : "+v"(lane), "+v"(tid), "+v"(a_even), "+v"(a_odd));
+        asm volatile("" : "+v"(trbase[0]), "+v"(trbase[1]), "+v"(trbase[2]), "+v"(trbase[3]));
+#pragma unroll
+        for (int r = 0; r < R; ++r) asm volatile("" : "+v"(dma_kk[r]));
+    };
+
     auto begin_segment = [&]() __attribute__((always_inline)) {
-        const uint16_t* qs = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)cc.s * Hq + head0 + c) * 576 + 8 * g4;
+        const uint16_t* qs = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)cc.s * Hq + head0 + (lane & 15)) * 576 +
+                             8 * (lane >> 4);
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
+        for (int ks = 0; ks < kKSteps; ++ks) qr[ks] = *reinterpret_cast<const uint4*>(qs + 32 * ks);
+        // Wait for the queries inside this branch: otherwise the compiler waits for all vector-memory
+        // operations where the branch rejoins, which on every step would drain the row prefetch.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        m = kNegInf;
+        l = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < kKSteps; ++ks)
-                qr[n][ks] = *reinterpret_cast<const uint4*>(qs + (size_t)n * 16 * 576 + 32 * ks);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            m[n] = kNegInf;
-            l[n] = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) O[n][q][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int dt = 0; dt < kDimTiles; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         pin_outputs();
         seg_from_start = cc.k == 0;
         if (seg_from_start && blockIdx.y == 0 && tid == 0) {
@@ -352,49 +431,50 @@ void decode_mla_kernel(MlaDecodeParams p) {
     };
 
     auto end_segment = [&]() __attribute__((always_inline)) {
+        const int c = lane & 15, g4 = lane >> 4;
         const bool whole = seg_from_start && cc.k + 1 == cc.nu;
-        float L[NT];
+        float L = l + __shfl_xor(l, 16);
+        L += __shfl_xor(L, 32);
+        // Output register j of a lane is head row 4 g4 + j; lane 4 g4 + j holds that row's (m, L).
+        float Lr[4], Mr[4];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            L[n] = l[n] + __shfl_xor(l[n], 16);
-            L[n] += __shfl_xor(L[n], 32);
+        for (int j = 0; j < 4; ++j) {
+            Lr[j] = __shfl(L, 4 * g4 + j);
+            Mr[j] = __shfl(m, 4 * g4 + j);
         }
+        const size_t row0 = (size_t)cc.s * Hq + head0 + 4 * g4;  // head row of register 0
+        if (whole) {
+            float inv[4];
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
+            for (int j = 0; j < 4; ++j) inv[j] = Lr[j] > 0.f ? 1.f / Lr[j] : 0.f;
+            uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row0 * 512 + c;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int hr = 4 * g4 + j;  // head row of output register j, = the lane holding its (m, l)
-                const float Lr = __shfl(L[n], hr);
-                const float Mr = __shfl(m[n], hr);
-                const int head = head0 + 16 * n + hr;
-                if (whole) {
-                    const float inv = Lr > 0.f ? 1.f / Lr : 0.f;
-                    uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + ((size_t)cc.s * Hq + head) * 512 + 8 * c;
+            for (int dt = 0; dt < kDimTiles; ++dt) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<uint4*>(o + 128 * q) =
-                            make_uint4(pack2<true>(O[n][q][0][j] * inv, O[n][q][1][j] * inv),
-                                       pack2<true>(O[n][q][2][j] * inv, O[n][q][3][j] * inv),
-                                       pack2<true>(O[n][q][4][j] * inv, O[n][q][5][j] * inv),
-                                       pack2<true>(O[n][q][6][j] * inv, O[n][q][7][j] * inv));
-                } else {
-                    const size_t idx = (size_t)(cc.s + w) * Hq + head;
-                    float* a = p.part_acc + idx * 512 + 8 * c;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        *reinterpret_cast<float4*>(a + 128 * q) =
-                            make_float4(O[n][q][0][j], O[n][q][1][j], O[n][q][2][j], O[n][q][3][j]);
-                        *reinterpret_cast<float4*>(a + 128 * q + 4) =
-                            make_float4(O[n][q][4][j], O[n][q][5][j], O[n][q][6][j], O[n][q][7][j]);
-                    }
-                    if (c == 0) *reinterpret_cast<float2*>(p.part_ml + idx * 2) = make_float2(Mr, Lr);
-                }
+                for (int j = 0; j < 4; ++j)
+                    o[j * 512 + 16 * dt] = (uint16_t)(pack2<true>(O[dt][j] * inv[j], 0.f) & 0xFFFFu);
+                __builtin_amdgcn_sched_barrier(0);  // one tile at a time (see the rescale)
             }
+        } else {
+            const size_t idx0 = row0 + (size_t)w * Hq;  // slot s + w
+            float* a = p.part_acc + idx0 * 512 + c;
+#pragma unroll
+            for (int dt = 0; dt < kDimTiles; ++dt) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[j * 512 + 16 * dt] = O[dt][j];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (c == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<float2*>(p.part_ml + (idx0 + j) * 2) = make_float2(Mr[j], Lr[j]);
+            }
+        }
     };
 
     // Scores, online softmax and PV of the unit in tile stage KT (validity vi), with the
     // dequantization of the next unit (raw stage KR2 -> tile stage KT2, validity vn) spread over the
-    // PV slots. Each slot loads the next slot's LDS operands and then issues its own products; the
+    // PV slots. Each slot loads the next slot's LDS operands, then issues its own products; the
     // scheduling barriers keep the compiler from hoisting every operand load to the top, which would
     // need more registers than the queries and outputs leave free.
     auto compute = [&](auto kt, int vi, auto kr2, auto kt2, int vn) __attribute__((always_inline)) {
@@ -402,33 +482,29 @@ void decode_mla_kernel(MlaDecodeParams p) {
         const char* tile = tile_stage<KT>();
         const int v = vi & 0xFF;
         const bool ok_a = vi & 0x100, ok_b = vi & 0x200;
+        const int g4 = lane >> 4;
 
-        // Scores: 36 A operands (t, ks), two per slot.
-        constexpr int kSlotsS = kKSteps;  // 2 * 18 operands / 2
-        f32x4_t S[2][NT];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int n = 0; n < NT; ++n) S[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        uint4 abuf[2][2];
-        auto load_a = [&](int slot, uint4 (&dst)[2]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int x = 2 * slot + h, t = x / kKSteps, ks = x % kKSteps;
-                dst[h] = *reinterpret_cast<const uint4*>(tile + ((ks & 1) ? a_odd : a_even) + t * kTile1 +
-                                                         (ks >> 1) * 128);
-            }
+        // The dequantization of the next unit starts with its LDS reads, whose results are used
+        // during PV.
+        ConvIn cin;
+        conv_load(kr2, cin);
+
+        // Scores: 36 A operands (t, ks), loaded kPre products ahead; two accumulator chains (t = 0, 1).
+        constexpr int kPre = 4;
+        constexpr int kA = 2 * kKSteps;
+        f32x4_t S[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        auto load_a = [&](int x) __attribute__((always_inline)) {
+            const int ks = x >> 1, t = x & 1;
+            return *reinterpret_cast<const uint4*>(tile + ((ks & 1) ? a_odd : a_even) + t * kTile1 + (ks >> 1) * 128);
         };
-        load_a(0, abuf[0]);
+        uint4 aring[kPre];
 #pragma unroll
-        for (int slot = 0; slot < kSlotsS; ++slot) {
-            if (slot + 1 < kSlotsS) load_a(slot + 1, abuf[(slot + 1) & 1]);
+        for (int i = 0; i < kPre; ++i) aring[i] = load_a(i);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int x = 2 * slot + h, t = x / kKSteps, ks = x % kKSteps;
-#pragma unroll
-                for (int n = 0; n < NT; ++n) S[t][n] = mfma_k32<true>(abuf[slot & 1][h], qr[n][ks], S[t][n]);
-            }
+        for (int x = 0; x < kA; ++x) {
+            const uint4 a = aring[x % kPre];
+            if (x + kPre < kA) aring[x % kPre] = load_a(x + kPre);
+            S[x & 1] = mfma_k32<true>(a, qr[x >> 1], S[x & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -438,87 +514,67 @@ void decode_mla_kernel(MlaDecodeParams p) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) ok[t][j] = 16 * t + g4 + 4 * j < v && (t == 0 ? ok_a : ok_b);
-        float tmax[NT];
-        bool need[NT];
-        bool any = false;
+        float mx = kNegInf;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            float mx = kNegInf;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int j = 0; j < 4; ++j) mx = ok[t][j] ? fmaxf(mx, S[t][j]) : mx;
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float tmax = mx * sl2;
+        const bool need = tmax > m + kRescaleSlack;
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+            const float mnew = need ? tmax : m;
+            const float alpha = need ? fast_exp2(m - mnew) : 1.f;
+            l *= alpha;
+            m = mnew;
+            const f32x4_t av = {__shfl(alpha, 4 * g4), __shfl(alpha, 4 * g4 + 1), __shfl(alpha, 4 * g4 + 2),
+                                __shfl(alpha, 4 * g4 + 3)};
+            // One output tile at a time: the scheduling barriers keep the compiler from reading all 128
+            // accumulators into vector registers at once.
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mx = ok[t][j] ? fmaxf(mx, S[t][n][j]) : mx;
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            tmax[n] = mx * sl2;
-            need[n] = tmax[n] > m[n] + kRescaleSlack;
-            any = any || need[n];
-        }
-        if (__builtin_amdgcn_ballot_w64(any) != 0) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const float mnew = need[n] ? tmax[n] : m[n];
-                const float alpha = need[n] ? fast_exp2(m[n] - mnew) : 1.f;
-                l[n] *= alpha;
-                m[n] = mnew;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float aj = __shfl(alpha, 4 * g4 + j);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) O[n][q][e][j] *= aj;
-                }
+            for (int dt = 0; dt < kDimTiles; ++dt) {
+                O[dt] *= av;
+                __builtin_amdgcn_sched_barrier(0);
             }
             pin_outputs();
         }
-        uint4 A[NT];
+        float pr[2][4];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            float pr[2][4];
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float ex = fast_exp2(fmaf(S[t][n][j], sl2, -m[n]));
-                    pr[t][j] = ok[t][j] ? ex : 0.f;
-                    l[n] += pr[t][j];
-                }
-            A[n] = make_uint4(pack2<true>(pr[0][0], pr[0][1]), pack2<true>(pr[0][2], pr[0][3]),
-                              pack2<true>(pr[1][0], pr[1][1]), pack2<true>(pr[1][2], pr[1][3]));
-        }
-
-        // PV: one slot per 128-dim latent quarter q. Lane c reads 8 dims (128q + 8c .. +7) of its eight
-        // rows; k-slot j of lane group g4 is token g4 + 4j (j < 4) or 16 + g4 + 4(j - 4).
-        constexpr int kSlotsP = 4;
-        constexpr int kConvPerSlot = (kLatentIters + kSlotsP - 1) / kSlotsP;
-        uint4 vbuf[2][2][4];
-        auto load_v = [&](int q, uint4 (&dst)[2][4]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    dst[t][i] = *reinterpret_cast<const uint4*>(tile + vbase[i] + t * kTile1 + q * 256);
-        };
-        load_v(0, vbuf[0]);
-#pragma unroll
-        for (int q = 0; q < kSlotsP; ++q) {
-            if (q + 1 < kSlotsP) load_v(q + 1, vbuf[(q + 1) & 1]);
-            const uint4 (&V)[2][4] = vbuf[q & 1];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? kSelHi : kSelLo;
-                auto wd = [&](const uint4& x) __attribute__((always_inline)) {
-                    return (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
-                };
-                const uint4 B = make_uint4(__builtin_amdgcn_perm(wd(V[0][1]), wd(V[0][0]), sel),
-                                           __builtin_amdgcn_perm(wd(V[0][3]), wd(V[0][2]), sel),
-                                           __builtin_amdgcn_perm(wd(V[1][1]), wd(V[1][0]), sel),
-                                           __builtin_amdgcn_perm(wd(V[1][3]), wd(V[1][2]), sel));
-#pragma unroll
-                for (int n = 0; n < NT; ++n) O[n][q][e] = mfma_k32<true>(A[n], B, O[n][q][e]);
+            for (int j = 0; j < 4; ++j) {
+                const float ex = fast_exp2(fmaf(S[t][j], sl2, -m));
+                pr[t][j] = ok[t][j] ? ex : 0.f;
+                l += pr[t][j];
             }
-            convert(kr2, kt2, vn, q * kConvPerSlot, std::integral_constant<int, kConvPerSlot>{}, q == kSlotsP - 1);
+        const uint4 A = make_uint4(pack2<true>(pr[0][0], pr[0][1]), pack2<true>(pr[0][2], pr[0][3]),
+                                   pack2<true>(pr[1][0], pr[1][1]), pack2<true>(pr[1][2], pr[1][3]));
+
+        // PV: one 16-dim output tile per product; its B operand is two transposed reads (tile rows
+        // 0..15 and 16..31). The dequantization of the next unit is spread over eight groups of four.
+        constexpr int kGroups = 8;
+        constexpr int kConvPerGroup = (kLatentIters + kGroups - 1) / kGroups;
+        auto load_b = [&](int dt) __attribute__((always_inline)) {
+            const char* base = tile + trbase[dt & 3] + (dt >> 2) * 128;
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(base));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(base + kTile1));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            return make_uint4(l2.x, l2.y, h2.x, h2.y);
+        };
+        uint4 bring[kPre];
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) bring[i] = load_b(i);
+#pragma unroll
+        for (int dt = 0; dt < kDimTiles; ++dt) {
+            const uint4 bop = bring[dt % kPre];
+            if (dt + kPre < kDimTiles) bring[dt % kPre] = load_b(dt + kPre);
+            O[dt] = mfma_k32<true>(A, bop, O[dt]);
+            if ((dt & 3) == 3)
+                conv_store(kr2, kt2, vn, cin, (dt >> 2) * kConvPerGroup, std::integral_constant<int, kConvPerGroup>{},
+                           dt == kDimTiles - 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -533,17 +589,20 @@ void decode_mla_kernel(MlaDecodeParams p) {
         compiler_fence();
         const int cur = info[K];
         const int nxt = info[(K + 1) & 3];
-        pin_registers();
+        pin_queries();
+        pin_outputs();
+        refresh_offsets();
         issue(std::integral_constant<int, K>{});
-        if (cc.g == g_begin || cc.k == 0) begin_segment();
+        if (__builtin_expect(cc.g == g_begin || cc.k == 0, 0)) begin_segment();
         compute(std::integral_constant<int, K & 1>{}, cur, std::integral_constant<int, (K + 1) & 3>{},
                 std::integral_constant<int, (K + 1) & 1>{}, nxt);
-        if (cc.g + 1 == g_end || cc.k + 1 == cc.nu) end_segment();
+        if (__builtin_expect(cc.g + 1 == g_end || cc.k + 1 == cc.nu, 0)) end_segment();
         advance(cc, p);
         return cc.g < g_end;
     };
 
     // Prologue: units 0..3 in flight, unit 0 dequantized.
+    prefetch_ids();
     issue(std::integral_constant<int, 0>{});
     issue(std::integral_constant<int, 1>{});
     issue(std::integral_constant<int, 2>{});
@@ -552,8 +611,12 @@ void decode_mla_kernel(MlaDecodeParams p) {
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    convert(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, info[0], 0,
-            std::integral_constant<int, kLatentIters>{}, true);
+    {
+        ConvIn cin;
+        conv_load(std::integral_constant<int, 0>{}, cin);
+        conv_store(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, info[0], cin, 0,
+                   std::integral_constant<int, kLatentIters>{}, true);
+    }
 
     while (true) {
         if (!step(std::integral_constant<int, 0>{})) break;
@@ -589,10 +652,10 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaDecodeParams p) {
 
 namespace {
 
-template <int NT, int NW>
+template <int NW>
 hipError_t launch_mla_typed(const MlaDecodeParams& p, hipStream_t stream) {
     const dim3 grid((unsigned)p.num_wgs, (unsigned)(p.num_q_heads / p.heads_per_wg));
-    hipLaunchKernelGGL((decode_mla_kernel<NT, NW>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((decode_mla_kernel<NW>), grid, dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -602,9 +665,9 @@ hipError_t launch_decode_mla(const MlaDecodeParams& p, hipStream_t stream) {
     if (p.num_seqs <= 0) return hipSuccess;
     hipError_t e;
     switch (p.heads_per_wg) {
-        case 64: e = launch_mla_typed<1, 4>(p, stream); break;
-        case 32: e = launch_mla_typed<1, 2>(p, stream); break;
-        case 16: e = launch_mla_typed<1, 1>(p, stream); break;
+        case 64: e = launch_mla_typed<4>(p, stream); break;
+        case 32: e = launch_mla_typed<2>(p, stream); break;
+        case 16: e = launch_mla_typed<1>(p, stream); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

@@ -430,7 +430,7 @@ int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const vo
     pp.scale_log2 = dp.scale_log2;
     pp.is_bf16 = dp.is_bf16;
     pp.group = dp.group;
-    pp.rows_per_item = 32;
+    pp.rows_per_item = 128;
     pp.total_q = total_q;
     if (max_query_len < 2) return PA_OK;
     return hip_status(pa::launch_prefill_chunk(pp, static_cast<hipStream_t>(stream)));

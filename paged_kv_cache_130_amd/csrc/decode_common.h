@@ -21,6 +21,29 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // accumulators always share the same reference.
 constexpr float kRescaleSlack = 8.f;
 
+// s_waitcnt immediate: wait until at most vm vector-memory operations are outstanding and all LDS
+// operations are done (expcnt not waited on).
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | ((vm >> 4) << 14); }
+
+// Read of a wave-uniform address through the constant address space, so that it becomes a scalar
+// load (counted by lgkmcnt). A vector load there would be counted by vmcnt, and waiting for it would
+// also wait for every direct-to-LDS copy issued before it. Only for data no kernel of the call writes.
+template <typename T>
+__device__ __forceinline__ T load_scalar(const T* ptr) {
+    return *(const __attribute__((address_space(4))) T*)ptr;
+}
+
+// Keeps the compiler from moving memory accesses across the hardware barrier next to it.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Work-group barrier for kernels that stage tiles with direct-to-LDS loads: the caller waits for its
+// own copies with s_waitcnt first. (__syncthreads would also wait for every copy still in flight.)
+__device__ __forceinline__ void lds_barrier() {
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
 // v_perm_b32 selectors: low 16-bit halves of (a, b) -> (a.lo, b.lo); high halves -> (a.hi, b.hi).
 constexpr uint32_t kSelLo = 0x05040100u;
 constexpr uint32_t kSelHi = 0x07060302u;

@@ -12,21 +12,25 @@
 // multiply-adds against 656 bytes read, about 425 flop per byte, above the MI355X bf16 ridge
 // (2.5 PFLOP/s over 8 TB/s, about 310). So the kernel is laid out for the matrix cores:
 //
-//  * A work-group owns up to 128 heads (4 waves x 32) and a balanced range of the token stream (all
-//    sequences' 32-token units, in order; ranges may cross sequences). Its waves hold their heads'
-//    queries (18 k-steps x 2 head tiles, 144 registers) and outputs (32 heads x 512 fp32, 256
-//    accumulation registers) for a whole segment, so the only operands streamed are K and V.
+//  * A work-group owns up to 64 heads (4 waves x 16; 128 heads take two head groups) and a balanced
+//    range of the token stream (all sequences' 32-token units, in order; ranges may cross
+//    sequences). Its waves hold their heads' queries (18 k-steps, 72 registers) and outputs
+//    (16 heads x 512 fp32, 128 accumulation registers) for a whole segment, so the only operands
+//    streamed are K and V. (32 heads per wave would halve the LDS traffic per head, but the compiler
+//    keeps every MFMA accumulator in the 256 accumulation registers, and 32 x 512 outputs fill them.)
 //  * Each 32-token unit is copied from HBM straight into LDS (global_load_lds, 16 bytes per lane,
-//    four stages in flight), then dequantized once for the whole work-group into a bf16 tile
+//    four stages in flight), then dequantized once per work-group into a bf16 tile
 //    [32 rows x (512 latent * scale | 64 RoPE)]: each e4m3 value is converted exactly to fp32,
 //    multiplied by its scale and rounded to bf16. Every wave reads its score (K) and PV (V) operands
-//    from that tile; rows are swizzled so the 16-byte operand reads are free of bank conflicts.
+//    from that tile; rows are swizzled so the operand reads are free of bank conflicts.
 //  * Scores S^T = K . Q^T and PV O += P . V run on v_mfma_f32_16x16x32_bf16. The score output
 //    registers are directly the PV A operand (token order sigma of mfma_common.h, two 16-token tiles
-//    per k=32 step); the V operand is gathered from the tile with v_perm_b32.
+//    per k=32 step); the V operand comes from ds_read_b64_tr_b16, which transposes 4 x 4 blocks of
+//    16-bit values across the lanes of a 16-lane group.
 //  * Per unit: one barrier; the dequantization of unit u+1 is interleaved with the products of
-//    unit u. The softmax is online (lazy reference, as in the dense decode) and a segment that is
-//    not a whole sequence writes an fp32 partial merged by mla_merge_kernel (log-sum-exp).
+//    unit u, and operands are loaded four products ahead. The softmax is online (lazy reference, as
+//    in the dense decode) and a segment that is not a whole sequence writes an fp32 partial merged
+//    by mla_merge_kernel (log-sum-exp).
 
 #include "decode_common.h"
 #include "mfma_common.h"
@@ -82,18 +86,6 @@ __device__ __forceinline__ char* tile_stage() {
 // 8..15) get eight different swizzles, and the rows g4 + 4i read for the value operand differ in
 // the swizzle's upper two bits.
 __device__ __forceinline__ int swz(int r) { return (((r >> 2) & 3) << 1) | (r & 1); }
-
-// s_waitcnt immediate: wait until at most vm vector-memory operations are outstanding and all LDS
-// operations are done (expcnt not waited on).
-constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | ((vm >> 4) << 14); }
-
-// Read of a wave-uniform address through the constant address space, so that it becomes a scalar
-// load (counted by lgkmcnt). A vector load here would be counted by vmcnt, and waiting for it would
-// also wait for every row copy issued before it. Only for data no kernel of the call writes.
-template <typename T>
-__device__ __forceinline__ T load_scalar(const T* ptr) {
-    return *(const __attribute__((address_space(4))) T*)ptr;
-}
 
 __device__ __forceinline__ int clamp_ctx(int64_t ctx, const MlaDecodeParams& p) {
     const int64_t cap = min((int64_t)p.max_context_len, (int64_t)p.bt_stride * p.block_size);
@@ -184,9 +176,6 @@ __device__ __forceinline__ uint4 dequant8(uint2 b, float sc) {
     return make_uint4(pack2<true>(a0.x * sc, a0.y * sc), pack2<true>(a1.x * sc, a1.y * sc),
                       pack2<true>(a2.x * sc, a2.y * sc), pack2<true>(a3.x * sc, a3.y * sc));
 }
-
-// Keeps the compiler from moving memory accesses across the hardware barrier next to it.
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 }  // namespace
 

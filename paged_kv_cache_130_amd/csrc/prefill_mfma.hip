@@ -8,16 +8,16 @@
 // those of paged decode ("deep dive into vLLM 05" §2; "KV Cache 与推理服务内存管理",
 // paged_attention), for every row of the chunk.
 //
-// Mapping: the rows of one K/V head are the (position, query head) pairs of the chunk, position-major.
-// A wave owns NT 16-row tiles of them, which share every K/V tile it loads. Per 16-token K/V tile and
-// row tile: S^T = K . Q^T on v_mfma_f32_16x16x32 (rows of Q are the B columns), causal and context
-// masks, lazily rescaled online softmax, and O += P . V on v_mfma_f32_16x16x16. The operand orders
-// are those of decode_mfma.hip (mfma_common.h). Sequences with a single query row are not handled
-// here: they are the decode rows of the call and go through the split-context decode kernels.
-//
-// Block ids come through a broadcast load issued two tiles ahead, and K/V tiles through register
-// prefetch one tile ahead. All loads are unconditional (past the end they read a cached query line),
-// so the in-order wait counts stay exact and two tiles are in flight while one is computed.
+// Mapping: the rows of one K/V head are the (position, query head) pairs of the chunk,
+// position-major. A work-group owns 128 of them (4 waves x two 16-row tiles) and walks the paged
+// context in 64-token K/V tiles, which its waves copy from HBM straight into LDS (global_load_lds,
+// two stages: the next tile is in flight while one is computed) and then share. Per tile and row
+// tile: S^T = K . Q^T on v_mfma_f32_16x16x32 (K from LDS, the rows' queries held in registers as the
+// B columns), causal and context masks, lazily rescaled online softmax, and O += P . V on
+// v_mfma_f32_16x16x32 with the value operand read through ds_read_b64_tr_b16 (the operand orders of
+// mfma_common.h; P in token order sigma is the A operand as it leaves the softmax). For bf16 the
+// probabilities go in as hi + lo pairs (pack2_split). Sequences with a single query row are not
+// handled here: they are the decode rows of the call and go through the split-context decode.
 
 #include "decode_common.h"
 #include "mfma_common.h"
@@ -69,36 +69,70 @@ __device__ __forceinline__ bool find_chunk_work(int w, const PrefillParams& p, i
 
 }  // namespace
 
-template <bool BF16, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(PrefillParams p) {
+constexpr int kPT = 64;                    // tokens per K/V tile
+constexpr int kPRow = kD * 2;              // bytes of one K/V head row
+constexpr int kPStage = kPT * kPRow;       // 16 KB
+constexpr int kPRows = 128;                // query rows per work-group
+
+// K and V tiles, two stages each, as separate objects (see decode_mla.hip: the compiler then tells
+// the stage being read from the one being filled by the direct-to-LDS copies).
+__shared__ __attribute__((aligned(16))) char s_pk0[kPStage];
+__shared__ __attribute__((aligned(16))) char s_pk1[kPStage];
+__shared__ __attribute__((aligned(16))) char s_pv0[kPStage];
+__shared__ __attribute__((aligned(16))) char s_pv1[kPStage];
+
+template <int K>
+__device__ __forceinline__ char* pk_stage() {
+    if constexpr (K == 0) return s_pk0;
+    else return s_pk1;
+}
+template <int K>
+__device__ __forceinline__ char* pv_stage() {
+    if constexpr (K == 0) return s_pv0;
+    else return s_pv1;
+}
+
+// Swizzle of the 16-byte chunks of tile row r (256-byte rows, a multiple of the 128-byte bank cycle):
+// the rows a group of eight lanes reads together for the score operand (sigma order) and the four
+// rows of a transposed value read get different chunks.
+__device__ __forceinline__ int pswz(int r) { return (((r >> 2) & 3) << 1) | (r & 1); }
+
+template <bool BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(PrefillParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4;
     const int c = lane & 15;
 
-    const int item = blockIdx.x * 4 + wave;
+    const int item = blockIdx.x;
     const int kvh = item % p.num_kv_heads;
     int s, rb;
-    if (!find_chunk_work(item / p.num_kv_heads, p, s, rb)) return;
+    if (!find_chunk_work(item / p.num_kv_heads, p, s, rb)) return;  // the same for the whole work-group
 
     const int G = p.group;
     const int bs = p.block_size;
+    const int bs_log2 = p.tiles_per_block_log2 + 4;
     const int q0 = __builtin_amdgcn_readfirstlane(p.query_start_loc[s]);
     const int qlen = __builtin_amdgcn_readfirstlane(chunk_len(s, p));
     const int64_t ncap = min((int64_t)p.max_seq_len, (int64_t)p.bt_stride * bs);
     const int n = (int)max((int64_t)0, min((int64_t)__builtin_amdgcn_readfirstlane(p.seq_lens[s]), ncap));
-    const int R = qlen * G;              // rows of this K/V head in this chunk
-    const int r0 = rb * 16 * NT;         // first row of this item
-    const int rend = min(R, r0 + 16 * NT);
-    const int a_max = n - qlen + (rend - 1) / G;  // causal limit of the item's last row
+    const int R = qlen * G;                                 // rows of this K/V head in this chunk
+    const int wg_r0 = rb * kPRows;
+    const int wg_rend = min(R, wg_r0 + kPRows);
+    const int wg_amax = n - qlen + (wg_rend - 1) / G;      // causal limit of the work-group's last row
+    const int r0 = wg_r0 + 32 * wave;                      // this wave's rows
+    const int rend = min(wg_rend, r0 + 32);
+    const int a_max = r0 < rend ? n - qlen + (rend - 1) / G : -1;
     const int hq0 = kvh * G;
+    const int ntiles = wg_amax >= 0 ? wg_amax / kPT + 1 : 0;
+    const int wave_tiles = a_max >= 0 ? a_max / kPT + 1 : 0;
 
-    // Per row tile: Q of row r0 + 16*nt + c as the B operand, and that row's causal limit.
+    // Per row tile: Q of row r0 + 16nt + c as the B operand, and that row's causal limit.
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(p.q);
-    uint4 qb[NT][4];
-    int alim[NT];
+    uint4 qb[2][4];
+    int alim[2];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < 2; ++nt) {
         const int r = r0 + 16 * nt + c;
         const bool valid = r < rend;
         const int pos = valid ? r / G : 0;
@@ -109,67 +143,141 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int ks = 0; ks < 4; ++ks)
             qb[nt][ks] = valid ? *reinterpret_cast<const uint4*>(qr + 32 * ks + 8 * g4) : make_uint4(0, 0, 0, 0);
     }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // queries in, before the copies start
 
-    const int tpb_log2 = p.tiles_per_block_log2;
-    const int tpb_mask = (1 << tpb_log2) - 1;
-    const int ntiles = a_max >= 0 ? (a_max + 16) >> 4 : 0;
-    const int last = ntiles - 1;
-    const int32_t* bt = p.block_tables + (size_t)s * p.bt_stride;
-    const int64_t krow = p.k_row_bytes, vrow = p.v_row_bytes;
-    const uint32_t klane = (uint32_t)(kvh * (kD * 2) + 16 * g4) + (uint32_t)sigma(c) * (uint32_t)krow;
-    const uint32_t vlane = (uint32_t)(kvh * (kD * 2) + 16 * c) + (uint32_t)g4 * (uint32_t)vrow;
-    const uint32_t nb = (uint32_t)p.num_blocks;
-    const char* dummy = reinterpret_cast<const char*>(qbase + (size_t)q0 * p.num_q_heads * kD);
-
-    // Block id of tile j, loaded by every lane from the same address (one cached line).
-    auto load_bid = [&](int j) { return bt[(j <= last ? j : 0) >> tpb_log2]; };
-    auto load = [&](uint4 (&kk)[4], uint4 (&vv)[4], int j, int phys) {
-        const bool real = j <= last;
-        phys = ((uint32_t)phys < nb) ? phys : 0;  // an out-of-range id is masked when the tile is used
-        const int64_t row0 = (int64_t)((j & tpb_mask) << 4);
-        const char* kt = real ? p.k + (int64_t)phys * p.k_block_stride + row0 * krow : dummy;
-        const char* vt = real ? p.v + (int64_t)phys * p.v_block_stride + row0 * vrow : dummy;
-        const int64_t kstep = real ? 64 : 0, vstep = real ? 4 * vrow : 0;
-        const uint32_t ko = real ? klane : 0u, vo = real ? vlane : 0u;
+    // Per-lane LDS offsets. Score operand: row 16sub + sigma(c), chunk 4ks + g4 (swizzled).
+    int a_off[4];
+    {
+        const int row = sigma(c);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            kk[i] = *reinterpret_cast<const uint4*>(kt + i * kstep + ko);
-            vv[i] = load_nt16(vt + i * vstep + vo);
+        for (int ks = 0; ks < 4; ++ks) a_off[ks] = row * kPRow + (((4 * ks + g4) ^ pswz(row)) << 4);
+    }
+    // Value operand through ds_read_b64_tr_b16 (see decode_mla.hip): lane c of lane group g4 supplies
+    // row 16sub + g4 + 4 (c >> 2), dims 16dt + 4 (c & 3) .. +3.
+    int trbase[4];
+    {
+        const int j = c >> 2, h = (c >> 1) & 1;
+#pragma unroll
+        for (int d3 = 0; d3 < 4; ++d3)
+            trbase[d3] = (g4 + 4 * j) * kPRow + ((2 * (d3 ^ j) + (h ^ (g4 & 1))) << 4) + ((c & 1) << 3);
+    }
+
+    // Copies: wave w loads tokens [16w, 16w + 16) of a tile, four rows per load instruction: lane i
+    // fills LDS chunk i % 16 of row 16w + 4r + i / 16 with global chunk (i % 16) ^ pswz(row).
+    const int64_t krow = p.k_row_bytes, vrow = p.v_row_bytes;
+    const uint32_t nb = (uint32_t)p.num_blocks;
+    const int32_t* bt = p.block_tables + (size_t)s * p.bt_stride;
+    const char* dummy = reinterpret_cast<const char*>(qbase);
+    int dma_row[4], dma_chunk[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        dma_row[r] = 16 * wave + 4 * r + (lane >> 4);
+        dma_chunk[r] = (lane & 15) ^ pswz(dma_row[r]);
+    }
+    // Block id of this wave's 16 tokens of tile j, and whether each 16-token group of the tile holds
+    // context tokens in a valid block (bit g).
+    auto group_id = [&](int j, int g) __attribute__((always_inline)) {
+        const int t = j * kPT + 16 * g;
+        return t < n ? load_scalar(bt + (t >> bs_log2)) : -1;
+    };
+    int pre_ok = 0, pre_phys = -1;  // the next tile to copy: validity bits, this wave's block
+    auto prefetch = [&](int j) __attribute__((always_inline)) {
+        pre_ok = 0;
+        pre_phys = -1;
+        if (j < ntiles) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int id = group_id(j, g);
+                if ((uint32_t)id < nb) pre_ok |= 1 << g;
+                if (g == wave) pre_phys = id;
+            }
         }
     };
-
-    float m[NT], l[NT];
-    f32x4_t O[NT][8];
+    int tile_ok[2] = {0, 0};
+    auto issue = [&](auto kst, int j) __attribute__((always_inline)) {
+        constexpr int K = decltype(kst)::value;
+        tile_ok[K] = pre_ok;
+        char* ks_ = pk_stage<K>();
+        char* vs_ = pv_stage<K>();
+        if (pre_ok & (1 << wave)) {
+            const int64_t phys = pre_phys;
+            const char* kb = p.k + phys * p.k_block_stride + (int64_t)kvh * kPRow;
+            const char* vb = p.v + phys * p.v_block_stride + (int64_t)kvh * kPRow;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row_in_block = (j * kPT + dma_row[r]) & (bs - 1);
+                const char* ksrc = kb + row_in_block * krow + dma_chunk[r] * 16;
+                const char* vsrc = vb + row_in_block * vrow + dma_chunk[r] * 16;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ksrc,
+                                                 (__attribute__((address_space(3))) void*)(ks_ + (16 * wave + 4 * r) * kPRow),
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vsrc,
+                                                 (__attribute__((address_space(3))) void*)(vs_ + (16 * wave + 4 * r) * kPRow),
+                                                 16, 0, 0);
+            }
+        } else {
+            // No context tokens here, or an invalid block id: the scores are masked; the value rows
+            // are zeroed so that masked probabilities (0) never meet NaN.
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<uint4*>(vs_ + dma_row[r] * kPRow + ((lane & 15) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    (void)dummy;
+
+    float m[2], l[2];
+    f32x4_t O[2][8];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
         m[nt] = kNegInf;
         l[nt] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) O[nt][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < 8; ++dt) O[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     const float sl2 = p.scale_log2;
 
-    auto step = [&](const uint4 (&kk)[4], uint4 (&vv)[4], int j, bool bad) {
-        const int t0 = j << 4;
-        const int nvalid = bad ? 0 : min(16, n - t0);  // tokens of this tile inside the context
-        bool inctx[4];
+    auto compute = [&](auto kst, int j) __attribute__((always_inline)) {
+        constexpr int K = decltype(kst)::value;
+        const char* kt = pk_stage<K>();
+        const char* vt = pv_stage<K>();
+        const int t0 = j * kPT;
+        const int okb = tile_ok[K];
+
+        // Scores for the four 16-token sub-tiles: all 16 K operands are loaded first, then the products
+        // run k-step by k-step over the eight (sub-tile, row tile) accumulators, so consecutive products
+        // are independent.
+        f32x4_t S[4][2];
+        uint4 abuf[4][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            inctx[i] = g4 + 4 * i < nvalid;
-            if (!inctx[i]) vv[i] = make_uint4(0u, 0u, 0u, 0u);  // rows past the context may hold NaN
-        }
+        for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < 4; ++ks)
+                abuf[sub][ks] = *reinterpret_cast<const uint4*>(kt + sub * 16 * kPRow + a_off[ks]);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) S = mfma_k32<BF16>(kk[ks], qb[nt][ks], S);
-            bool ok[4];
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) S[sub][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) S[sub][nt] = mfma_k32<BF16>(abuf[sub][ks], qb[nt][ks], S[sub][nt]);
+
+        // Register jj of sub-tile sub holds token t0 + 16 sub + g4 + 4 jj of row c.
+        uint4 Ahi[2][2], Alo[2][2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            bool ok[4][4];
             float mx = kNegInf;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                ok[jj] = inctx[jj] && (t0 + g4 + 4 * jj <= alim[nt]);  // causal: token <= position
-                mx = ok[jj] ? fmaxf(mx, S[jj]) : mx;
-            }
+            for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int t = t0 + 16 * sub + g4 + 4 * jj;
+                    ok[sub][jj] = ((okb >> sub) & 1) && t <= alim[nt];
+                    mx = ok[sub][jj] ? fmaxf(mx, S[sub][nt][jj]) : mx;
+                }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float tmax = mx * sl2;
@@ -179,56 +287,105 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 const float alpha = need ? fast_exp2(m[nt] - mnew) : 1.f;
                 l[nt] *= alpha;
                 m[nt] = mnew;
+                const f32x4_t av = {__shfl(alpha, 4 * g4), __shfl(alpha, 4 * g4 + 1), __shfl(alpha, 4 * g4 + 2),
+                                    __shfl(alpha, 4 * g4 + 3)};
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) O[nt][dt] *= av;
+            }
+            float pr[4][4];
+#pragma unroll
+            for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const float a = __shfl(alpha, 4 * g4 + jj);
+                    const float ex = fast_exp2(fmaf(S[sub][nt][jj], sl2, -m[nt]));
+                    pr[sub][jj] = ok[sub][jj] ? ex : 0.f;
+                    l[nt] += pr[sub][jj];
+                }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) O[nt][e][jj] *= a;
+            for (int h = 0; h < 2; ++h) {
+                uint32_t hw[4], lw[4];
+                pack2_split<BF16>(pr[2 * h][0], pr[2 * h][1], hw[0], lw[0]);
+                pack2_split<BF16>(pr[2 * h][2], pr[2 * h][3], hw[1], lw[1]);
+                pack2_split<BF16>(pr[2 * h + 1][0], pr[2 * h + 1][1], hw[2], lw[2]);
+                pack2_split<BF16>(pr[2 * h + 1][2], pr[2 * h + 1][3], hw[3], lw[3]);
+                Ahi[nt][h] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                Alo[nt][h] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            }
+        }
+
+        // PV over the two 32-token halves h: B operand of dims [16dt, 16dt + 16) is two transposed
+        // reads (sub-tiles 2h and 2h + 1).
+        auto load_b = [&](int h, int dt) __attribute__((always_inline)) {
+            const char* base = vt + trbase[dt & 3] + (dt >> 2) * 128 + 2 * h * 16 * kPRow;
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(base));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(base + 16 * kPRow));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            return make_uint4(l2.x, l2.y, h2.x, h2.y);
+        };
+        // Loaded two products ahead; the lo products of a tile run one output tile behind its hi
+        // products, so no two consecutive products share an accumulator.
+        uint4 bq[4];  // ring: slot x % 4 holds product x's operand until its lo product is issued
+        bq[0] = load_b(0, 0);
+        bq[1] = load_b(0, 1);
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const int h = x >> 3, dt = x & 7;
+            if (x + 2 < 16) bq[(x + 2) % 4] = load_b((x + 2) >> 3, (x + 2) & 7);
+            const uint4 B = bq[x % 4];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) O[nt][dt] = mfma_k32<BF16>(Ahi[nt][h], B, O[nt][dt]);
+            if constexpr (BF16) {
+                if (x > 0) {
+                    const int hp = (x - 1) >> 3, dp = (x - 1) & 7;
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) O[nt][dp] = mfma_k32<BF16>(Alo[nt][hp], bq[(x - 1) % 4], O[nt][dp]);
                 }
             }
-            float pr[4];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (BF16) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const float ex = fast_exp2(fmaf(S[jj], sl2, -m[nt]));
-                pr[jj] = ok[jj] ? ex : 0.f;
-                l[nt] += pr[jj];
-            }
-            uint2 A, Alo;
-            pack2_split<BF16>(pr[0], pr[1], A.x, Alo.x);
-            pack2_split<BF16>(pr[2], pr[3], A.y, Alo.y);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint2 B = v_operand(vv, e);
-                O[nt][e] = mfma_k16<BF16>(A, B, O[nt][e]);
-                if constexpr (BF16) O[nt][e] = mfma_k16<BF16>(Alo, B, O[nt][e]);
-            }
+            for (int nt = 0; nt < 2; ++nt) O[nt][7] = mfma_k32<BF16>(Alo[nt][1], bq[15 % 4], O[nt][7]);
         }
     };
 
+    auto step = [&](auto kst, int j) __attribute__((always_inline)) {
+        constexpr int K = decltype(kst)::value;
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // this wave's copies of tile j are in
+        lds_barrier();                                      // everyone's are; tile j - 1 is done
+        if (j * kPT + kPT > n) {
+            // The last tile reaches past the context: zero the value rows past it (the copies brought
+            // whatever the block holds there).
+            char* vs_ = pv_stage<K>();
+            for (int x = threadIdx.x; x < kPT * 16; x += 256) {
+                const int row = x >> 4;
+                if (j * kPT + row >= n) *reinterpret_cast<uint4*>(vs_ + row * kPRow + ((x & 15) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+            }
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+            lds_barrier();
+        }
+        if (j + 1 < ntiles) issue(std::integral_constant<int, K ^ 1>{}, j + 1);
+        if (j < wave_tiles) compute(kst, j);
+        // The block ids of tile j + 2, read after the products: scalar loads share their wait counter
+        // with LDS reads, so issued before the score phase they would stall its first LDS wait.
+        prefetch(j + 2);
+    };
+
     if (ntiles > 0) {
-        uint4 k0[4], v0[4], k1[4], v1[4];
-        int bid_a = load_bid(0);
-        int phys0 = __builtin_amdgcn_readfirstlane(bid_a);
-        int bid_b = load_bid(1);
-        load(k0, v0, 0, phys0);
-        bool bad0 = (uint32_t)phys0 >= nb, bad1 = false;
+        prefetch(0);
+        issue(std::integral_constant<int, 0>{}, 0);
+        prefetch(1);
         for (int j = 0; j < ntiles; j += 2) {
-            bid_a = load_bid(j + 2);
-            const int phys1 = __builtin_amdgcn_readfirstlane(bid_b);
-            bad1 = (uint32_t)phys1 >= nb;
-            load(k1, v1, j + 1, phys1);
-            step(k0, v0, j, bad0);
-            bid_b = load_bid(j + 3);
-            const int phys2 = __builtin_amdgcn_readfirstlane(bid_a);
-            bad0 = (uint32_t)phys2 >= nb;
-            load(k0, v0, j + 2, phys2);
-            if (j + 1 < ntiles) step(k1, v1, j + 1, bad1);
+            step(std::integral_constant<int, 0>{}, j);
+            if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
         }
     }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < 2; ++nt) {
         float lt = l[nt];
         lt += __shfl_xor(lt, 16);
         lt += __shfl_xor(lt, 32);
@@ -240,30 +397,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             const int pos = r / G;
             const int head = r - pos * G;
             const float inv = L > 0.f ? 1.f / L : 0.f;  // no visible token (inconsistent lengths): output 0
-            uint4 o;
-            o.x = pack2<BF16>(O[nt][0][jj] * inv, O[nt][1][jj] * inv);
-            o.y = pack2<BF16>(O[nt][2][jj] * inv, O[nt][3][jj] * inv);
-            o.z = pack2<BF16>(O[nt][4][jj] * inv, O[nt][5][jj] * inv);
-            o.w = pack2<BF16>(O[nt][6][jj] * inv, O[nt][7][jj] * inv);
-            *reinterpret_cast<uint4*>(out + ((size_t)(q0 + pos) * p.num_q_heads + hq0 + head) * kD + c * 8) = o;
+            uint16_t* o = out + ((size_t)(q0 + pos) * p.num_q_heads + hq0 + head) * kD + c;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[16 * dt] = (uint16_t)(pack2<BF16>(O[nt][dt][jj] * inv, 0.f) & 0xFFFFu);
         }
     }
 }
 
 hipError_t launch_prefill_chunk(const PrefillParams& p, hipStream_t stream) {
     if (p.num_seqs <= 0) return hipSuccess;
-    // Upper bound of the work items: every sequence's rows rounded up to whole items.
-    const int64_t items = ((int64_t)p.max_query_len * p.group + p.rows_per_item - 1) / p.rows_per_item;
-    const int64_t waves = items * p.num_seqs * p.num_kv_heads;
-    const int64_t bound = ((int64_t)p.total_q * p.group + p.rows_per_item - 1) / p.rows_per_item +
-                          p.num_seqs;  // sum of per-sequence item counts is at most this
-    const int64_t w = min(waves, bound * p.num_kv_heads);
-    const int64_t wgs = (w + 3) / 4;
+    // Upper bound of the work-groups: every sequence's rows rounded up to whole row blocks.
+    const int64_t per_seq = ((int64_t)p.max_query_len * p.group + p.rows_per_item - 1) / p.rows_per_item;
+    const int64_t bound = ((int64_t)p.total_q * p.group + p.rows_per_item - 1) / p.rows_per_item + p.num_seqs;
+    const int64_t wgs = min(per_seq * p.num_seqs, bound) * p.num_kv_heads;
     if (wgs <= 0) return hipSuccess;
     if (p.is_bf16)
-        hipLaunchKernelGGL((prefill_mfma_kernel<true, 2>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((prefill_mfma_kernel<true>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_mfma_kernel<false, 2>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((prefill_mfma_kernel<false>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -75,30 +75,66 @@ __device__ __forceinline__ int query_row(int s, const DenseDecodeParams& p) {
     return p.query_start_loc != nullptr ? __builtin_amdgcn_readfirstlane(p.query_start_loc[s]) : s;
 }
 
-// Sum over the wave of min(nparts(s), cap) for all sequences (cap = max_parts gives the total).
-__device__ __forceinline__ int count_below(int cap, const DenseDecodeParams& p, int lane) {
-    int c = 0;
-    for (int s = lane; s < p.num_seqs; s += 64) c += min(parts_of(s, p), cap);
-    return __builtin_amdgcn_readfirstlane((int)group_sum<64>((float)c));
-}
-
 // Work item w of the partition-major list -> (sequence, partition). Returns false past the end.
 // C(q) = sum_s min(nparts(s), q) counts the items of partitions below q; item w lies in the partition
 // p with C(p) <= w < C(p+1), and is the (w - C(p))-th sequence (in order) that has more than p
 // partitions. Counts stay far below 2^24, so the float reductions are exact.
+//
+// With up to 256 sequences the partition counts of all of them are read once into registers
+// (sequence 64k + lane in register k), with every load issued before the first wait, so the search
+// costs one memory round trip and then only register arithmetic. With more sequences the counts
+// are re-read for every step of the search.
 __device__ __forceinline__ bool find_work(int w, const DenseDecodeParams& p, int& s_out, int& part_out) {
+    constexpr int NC = 4;
     const int lane = threadIdx.x & 63;
-    if (w >= count_below(p.max_parts, p, lane)) return false;
+    const bool fast = p.num_seqs <= 64 * NC;
+    int pv[NC];
+    if (fast) {
+        const bool mixed = p.query_start_loc != nullptr;
+        const int32_t* qsl = mixed ? p.query_start_loc : p.context_lens;  // any valid address if not mixed
+        int cl[NC], q0[NC], q1[NC];
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const int s = min(64 * k + lane, p.num_seqs - 1);
+            cl[k] = p.context_lens[s];
+            q0[k] = qsl[s];
+            q1[k] = qsl[mixed ? s + 1 : s];
+        }
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const int ctx = clamp_context(cl[k], p);
+            const int n = ctx == 0 ? 1 : (ctx + p.partition_tokens - 1) / p.partition_tokens;
+            pv[k] = (64 * k + lane < p.num_seqs && (!mixed || q1[k] - q0[k] == 1)) ? n : 0;
+        }
+    }
+    auto count_below = [&](int cap) __attribute__((always_inline)) {
+        int c = 0;
+        if (fast) {
+#pragma unroll
+            for (int k = 0; k < NC; ++k) c += min(pv[k], cap);
+        } else {
+            for (int s = lane; s < p.num_seqs; s += 64) c += min(parts_of(s, p), cap);
+        }
+        return __builtin_amdgcn_readfirstlane((int)group_sum<64>((float)c));
+    };
+    if (w >= count_below(p.max_parts)) return false;
     int lo = 0, hi = p.max_parts;  // C(lo) <= w < C(hi)
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (count_below(mid, p, lane) <= w) lo = mid;
+        if (count_below(mid) <= w) lo = mid;
         else hi = mid;
     }
-    int r = w - count_below(lo, p, lane);  // rank among sequences with more than lo partitions
+    int r = w - count_below(lo);  // rank among sequences with more than lo partitions
     for (int base = 0; base < p.num_seqs; base += 64) {
         const int s = base + lane;
-        const bool has = s < p.num_seqs && parts_of(s, p) > lo;
+        int n = 0;
+        if (fast) {
+#pragma unroll
+            for (int k = 0; k < NC; ++k) n = (base >> 6) == k ? pv[k] : n;
+        } else {
+            n = s < p.num_seqs ? parts_of(s, p) : 0;
+        }
+        const bool has = n > lo;
         const uint64_t mask = __builtin_amdgcn_ballot_w64(has);
         const int cnt = __builtin_popcountll(mask);
         if (r < cnt) {

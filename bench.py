@@ -306,7 +306,7 @@ def run_mla(steps, warmup):
         "mla_hbm_frac": kv / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
                      "frac": tf / MFMA_BF16_PEAK_TF, "traffic": traffic_for("dsa_mla"),
-                     "kernel": "pa_decode (decode_mla_kernel + decode_reduce_kernel)",
+                     "kernel": "pa_decode (decode_mla_kernel + mla_merge_kernel)",
                      "algorithmic_flops_per_call": flops, "algorithmic_bytes_per_call": kv},
         "sum_context_tokens": sum_ctx,
     }

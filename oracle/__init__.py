@@ -14,6 +14,8 @@ kernel error. It computes:
 * ``paging``: blocks per sequence, slot integers, the cache-view byte
   address, and the stride rules of the layer-outer and block-outer layouts.
 * ``cache_write``: the ``reshape_and_cache`` scatter, as bytes.
+* ``quant``: quantize-on-write of the DSA dual cache rows (bf16 in, packed
+  fp8 rows with float32 group scales out), then the same scatter.
 * ``attention``: paged decode (dense and grouped heads), causal chunks over
   paged context, MLA latent decode, and the log-sum-exp merge of
   split-context partials.
@@ -30,4 +32,4 @@ the pages' worked numbers, closed forms, torch library routines, or brute
 force. No function is parity-unpinned.
 """
 
-from . import numerics, paging, cache_write, attention  # noqa: F401
+from . import numerics, paging, cache_write, attention, quant  # noqa: F401

@@ -77,3 +77,37 @@ def test_write_at_wrong_row_is_caught(monkeypatch):
     orig = P.address
     monkeypatch.setattr(P, "address", lambda v, layer, b, pos: orig(v, layer, b, (pos + 1) % 16))
     _fails(TW.test_round_trip_and_untouched_bytes)
+
+
+def test_truncating_fp8_encoder_is_caught(monkeypatch):
+    from oracle import quant as Q
+    import test_oracle_quant as TQ
+    table = Q._POS_VALUES
+
+    def truncating(q):
+        q = np.asarray(q, dtype=np.float64)
+        a = np.abs(q)
+        idx = np.searchsorted(table, a, side="right") - 1       # round toward zero
+        code = Q._POS_CODES[idx.clip(0, len(table) - 1)]
+        return (code | np.where(np.signbit(q), 0x80, 0)).astype(np.uint8)
+    monkeypatch.setattr(Q, "e4m3_encode", truncating)
+    _fails(TQ.test_random_values_match_torch)
+
+
+def test_wrong_fp8_scale_divisor_is_caught(monkeypatch):
+    from oracle import quant as Q
+    import test_oracle_quant as TQ
+    monkeypatch.setattr(Q, "E4M3_MAX", 480.0)
+    _fails(TQ.test_group_recipe_matches_torch, "normal")
+
+
+def test_shifted_scale_group_is_caught(monkeypatch):
+    from oracle import quant as Q
+    import test_oracle_quant as TQ
+    orig = Q.quantize_group
+
+    def shifted(bits):                      # groups of 128 starting one value late
+        bits = np.asarray(bits, dtype=np.uint16)
+        return orig(np.roll(bits, 1))
+    monkeypatch.setattr(Q, "quantize_group", shifted)
+    _fails(TQ.test_row_layout_matches_page_byte_counts)

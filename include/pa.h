@@ -152,6 +152,35 @@ int32_t pa_reshape_and_cache(const void* k, int64_t k_pitch, const void* v, int6
                              void* v_cache, int64_t v_cache_bytes, pa_cache_view v_view,
                              int32_t layer, int32_t block_size, int64_t num_blocks, void* stream);
 
+/* pa_quantize_and_cache_mla: quantize-on-write of the DSA dual cache through one slot_mapping.
+ *
+ * [MEM] §3.4: the cache may be stored at low precision by quantizing as it is written (FP8 being the
+ * safest format) and dequantizing as it is read; finer scale groups are more accurate. [LAYOUT]
+ * (two caches sharing one block table) fixes the rows: an MLA row is 512 B of FP8 latent, 16 B of
+ * scale and 128 B of BF16 RoPE (656 B); an indexer row is 128 B of FP8 key and a 4 B FP32 scale
+ * (132 B). Per group of 128 values (latent values [128k, 128k+128) share scale k; the indexer key has
+ * one group): scale = amax / 448 in float32, and each value x is stored as the OCP E4M3 code (bias 7,
+ * max 448) nearest to x / scale (float32 division), ties to the even mantissa, with the quotient's
+ * sign, saturating at 448. A group of zeros stores scale 0 and zero codes. The rows are then
+ * written exactly as pa_reshape_and_cache writes them, and pa_decode reads the MLA view.
+ *
+ *   latent         device bf16 [num_tokens, 512]; row t at latent + t*latent_pitch (bytes).
+ *   rope           device bf16 [num_tokens, 64], copied unchanged into bytes [528, 656) of the row.
+ *   index_key      device bf16 [num_tokens, 128], or NULL to write only the MLA view.
+ *   slot_mapping   device int64 [num_tokens]; negative slots are skipped, as in pa_reshape_and_cache.
+ *   mla_cache, index_cache  device allocation bases (may be the same allocation, as in [LAYOUT]'s
+ *                  dual cache); *_cache_bytes give their sizes for the extent check.
+ *   mla_view       row_bytes must be 656; index_view row_bytes must be 132.
+ * Inputs must be finite (otherwise the rows are unspecified). Alignment: latent, rope, index_key
+ * and their pitches 16 bytes; mla_cache and the MLA view 16 bytes; index_cache and the index view
+ * 4 bytes. num_tokens == 0 is a no-op. */
+int32_t pa_quantize_and_cache_mla(const void* latent, int64_t latent_pitch, const void* rope, int64_t rope_pitch,
+                                  const void* index_key, int64_t index_pitch, const int64_t* slot_mapping,
+                                  int32_t num_tokens, void* mla_cache, int64_t mla_cache_bytes,
+                                  pa_cache_view mla_view, void* index_cache, int64_t index_cache_bytes,
+                                  pa_cache_view index_view, int32_t layer, int32_t block_size,
+                                  int64_t num_blocks, void* stream);
+
 /* Workspace bytes pa_decode needs for this shape (0 when no split-context partials are needed). */
 size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t max_context_len);
 

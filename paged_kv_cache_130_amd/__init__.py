@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     pa_decode_workspace_bytes,
     pa_prefill_chunk,
     pa_prefill_workspace_bytes,
+    pa_quantize_and_cache_mla,
     pa_reshape_and_cache,
     status_string,
 )

@@ -28,7 +28,7 @@ PA_KV_F16 = 0
 PA_KV_BF16 = 1
 PA_KV_MLA656_E4M3 = 2
 
-EXPORTS = ("pa_abi_version", "pa_status_string", "pa_last_hip_error", "pa_reshape_and_cache",
+EXPORTS = ("pa_abi_version", "pa_status_string", "pa_last_hip_error", "pa_reshape_and_cache", "pa_quantize_and_cache_mla",
            "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_workspace_bytes", "pa_prefill_chunk")
 
 
@@ -70,6 +70,8 @@ def _load():
         "pa_status_string": (ctypes.c_char_p, [I32]),
         "pa_last_hip_error": (I32, []),
         "pa_reshape_and_cache": (I32, [P, I64, P, I64, P, I32, P, I64, V, P, I64, V, I32, I32, I64, P]),
+        "pa_quantize_and_cache_mla": (I32, [P, I64, P, I64, P, I64, P, I32, P, I64, V, P, I64, V, I32, I32, I64,
+                                            P]),
         "pa_decode_workspace_bytes": (SZ, [ctypes.POINTER(pa_attn_desc), I32, I32]),
         "pa_decode": (I32, [P, P, P, P, P, I32, P, I32, I32, ctypes.c_float, ctypes.POINTER(pa_attn_desc), P, SZ,
                             P]),
@@ -201,6 +203,29 @@ def pa_reshape_and_cache(k, slot_mapping, k_cache, k_view: CacheView, layer: int
                                    k_view.c(), _ptr(v_cache), _nbytes(v_cache) if v_cache is not None else 0, vv,
                                    layer, block_size, num_blocks, _stream(stream))
     _check("pa_reshape_and_cache", st)
+
+
+def pa_quantize_and_cache_mla(latent, rope, slot_mapping, mla_cache, mla_view: CacheView, layer: int,
+                              block_size: int, num_blocks: int, index_key=None, index_cache=None,
+                              index_view: CacheView | None = None, stream=None):
+    """Quantize bf16 latent [T, 512] + RoPE [T, 64] (and indexer key [T, 128]) into the fp8 dual-cache rows."""
+    _require_device(latent, rope, slot_mapping, mla_cache, index_key, index_cache)
+    if slot_mapping.dtype.itemsize != 8 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 tensor")
+    T = slot_mapping.numel()
+
+    def pitch(x, cols):
+        if x.dim() != 2 or x.shape[1] != cols or x.element_size() != 2 or x.stride(1) != 1 or x.shape[0] < T:
+            raise ValueError(f"expected a [>= {T}, {cols}] 16-bit tensor with unit column stride")
+        return x.stride(0) * 2
+    lp, rp = pitch(latent, 512), pitch(rope, 64)
+    ip = pitch(index_key, 128) if index_key is not None else 0
+    iv = index_view.c() if index_view is not None else pa_cache_view(0, 0, 0, 0, 0)
+    st = _lib.pa_quantize_and_cache_mla(_ptr(latent), lp, _ptr(rope), rp, _ptr(index_key), ip, _ptr(slot_mapping), T,
+                                        _ptr(mla_cache), _nbytes(mla_cache), mla_view.c(), _ptr(index_cache),
+                                        _nbytes(index_cache) if index_cache is not None else 0, iv, layer,
+                                        block_size, num_blocks, _stream(stream))
+    _check("pa_quantize_and_cache_mla", st)
 
 
 def pa_decode_workspace_bytes(desc: AttnDesc, num_seqs: int, max_context_len: int) -> int:

@@ -90,6 +90,7 @@ int32_t check_dense_desc(const pa_attn_desc& d) {
 }
 
 constexpr int32_t kMlaRowBytes = 656;  // 512 e4m3 latent + 4 float32 scales + 64 bf16 RoPE
+constexpr int32_t kIndexRowBytes = 132;  // 128 e4m3 key values + 1 float32 scale
 constexpr int32_t kMlaUnit = 32;       // tokens per MLA work unit
 
 int32_t check_mla_desc(const pa_attn_desc& d) {
@@ -224,6 +225,52 @@ int32_t pa_reshape_and_cache(const void* k, int64_t k_pitch, const void* v, int6
     p.block_size = block_size;
     p.num_slots = num_blocks * block_size;
     return hip_status(pa::launch_cache_write(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_quantize_and_cache_mla(const void* latent, int64_t latent_pitch, const void* rope, int64_t rope_pitch,
+                                  const void* index_key, int64_t index_pitch, const int64_t* slot_mapping,
+                                  int32_t num_tokens, void* mla_cache, int64_t mla_cache_bytes, pa_cache_view mla_view,
+                                  void* index_cache, int64_t index_cache_bytes, pa_cache_view index_view,
+                                  int32_t layer, int32_t block_size, int64_t num_blocks, void* stream) {
+    if (num_tokens < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return PA_OK;
+    if (!latent || !rope || !slot_mapping || !mla_cache) return PA_ERR_NULL_POINTER;
+    if (index_key && !index_cache) return PA_ERR_NULL_POINTER;
+    if (block_size <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_blocks > INT64_MAX / block_size) return PA_ERR_INVALID_ARGUMENT;
+    if (mla_view.row_bytes != kMlaRowBytes) return PA_ERR_INVALID_ARGUMENT;
+    if (latent_pitch < 512 * 2 || rope_pitch < 64 * 2) return PA_ERR_INVALID_ARGUMENT;
+    int32_t st = check_view(mla_view, layer, num_blocks, block_size, mla_cache_bytes);
+    if (st != PA_OK) return st;
+    if (!aligned(latent, 16) || !aligned(rope, 16) || !aligned(latent_pitch, 16) || !aligned(rope_pitch, 16) ||
+        !aligned(mla_cache, 16) || !view_aligned(mla_view, layer, 16))
+        return PA_ERR_MISALIGNED;
+    pa::QuantWriteParams p;
+    std::memset(&p, 0, sizeof(p));
+    if (index_key) {
+        if (index_view.row_bytes != kIndexRowBytes) return PA_ERR_INVALID_ARGUMENT;
+        if (index_pitch < 128 * 2) return PA_ERR_INVALID_ARGUMENT;
+        st = check_view(index_view, layer, num_blocks, block_size, index_cache_bytes);
+        if (st != PA_OK) return st;
+        if (!aligned(index_key, 16) || !aligned(index_pitch, 16) || !aligned(index_cache, 4) ||
+            !view_aligned(index_view, layer, 4))
+            return PA_ERR_MISALIGNED;
+        p.index_key = static_cast<const char*>(index_key);
+        p.index_pitch = index_pitch;
+        p.idx_dst = static_cast<char*>(index_cache) + index_view.offset + (int64_t)layer * index_view.layer_stride;
+        p.idx_block_stride = index_view.block_stride;
+    }
+    p.latent = static_cast<const char*>(latent);
+    p.latent_pitch = latent_pitch;
+    p.rope = static_cast<const char*>(rope);
+    p.rope_pitch = rope_pitch;
+    p.slots = slot_mapping;
+    p.mla_dst = static_cast<char*>(mla_cache) + mla_view.offset + (int64_t)layer * mla_view.layer_stride;
+    p.mla_block_stride = mla_view.block_stride;
+    p.num_slots = num_blocks * block_size;
+    p.num_tokens = num_tokens;
+    p.block_size = block_size;
+    return hip_status(pa::launch_quant_cache_write(p, static_cast<hipStream_t>(stream)));
 }
 
 size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t max_context_len) {

@@ -45,6 +45,167 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Quantize-on-write for the DSA dual cache.
+//
+// "deep dive into vLLM 05" §3.4: the cache can be quantized as it is written and dequantized as it
+// is read, FP8 being the safest format; finer scale groups are more accurate. "vLLM KV Cache Layout
+// 可视化" (two caches sharing one block table) fixes the rows: 512 B FP8 latent + 16 B scale + 128 B
+// BF16 RoPE per MLA token, 128 B FP8 key + 4 B FP32 scale per indexer token. Per group of 128 values
+// (4 latent groups, 1 indexer group): scale = amax / 448 in float32, and each value is stored as the
+// OCP E4M3 code nearest to x / scale (float32 division), ties to the even mantissa, saturating at
+// 448; a group of zeros stores scale 0 and zero codes.
+//
+// A 16-lane DPP row holds one group (8 values per lane, 16 bytes of bf16), so the group maximum is a
+// 4-step row reduction. blockIdx.y = 0 writes MLA rows: a wave takes several tokens in turn, its 4
+// DPP rows being the 4 groups of a token (lanes 0..7 also move the 128 RoPE bytes unchanged);
+// blockIdx.y = 1 writes indexer rows, 4 tokens per step (one token per DPP row). The quotient is clamped to +-448 and converted by
+// v_cvt_pk_fp8_f32 (OCP E4M3, round to nearest even): after the clamp every quotient lies inside the
+// format's range, where that conversion is exactly the nearest-even rounding the rows are defined by
+// (quotients between 448 and 464 round to 448 either way).
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Largest magnitude over the 16 lanes of a DPP row; every lane of the row gets it.
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_mov<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp_mov<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp_mov<kDppRowHalfMirror>(x));
+    x = fmaxf(x, dpp_mov<kDppRowMirror>(x));
+    return x;
+}
+
+// 16 bytes of bf16 -> 8 fp32 values (exact), the largest magnitude among them.
+__device__ __forceinline__ float load_bf16x8(const char* src, float (&x)[8]) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        amax = fmaxf(amax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
+    }
+    return amax;
+}
+
+// Codes of 8 values of one group given the group's scale; a zero scale (all-zero group) gives zero
+// codes.
+//
+// The quotients x / scale must be the correctly rounded float32 ones. One correctly rounded division
+// gives y = 1 / scale for the group; then per value q0 = x * y is within one unit in the last place
+// of x / scale, the remainder x - q0 * scale is exact in one fma, and q0 + remainder * y (one more
+// fma) is the correctly rounded quotient (Markstein's correction for round-to-nearest, valid while
+// nothing overflows; the quotients here are at most 448 in magnitude, and results too small for
+// normal float32 are far below the smallest E4M3 step, so they encode as zero either way). A scale
+// below the smallest normal float32 (a group whose largest value is below about 5e-36) would make
+// 1 / scale overflow; such groups divide each value directly.
+__device__ __forceinline__ uint2 quantize8(const float (&x)[8], float scale) {
+    uint32_t w[2] = {0u, 0u};
+    if (scale > 0.f) {
+        const bool normal = scale >= 1.17549435e-38f;
+        const float y = __fdiv_rn(1.f, normal ? scale : 1.f);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float q[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float qq;
+                if (normal) {
+                    const float q0 = x[4 * h + i] * y;
+                    const float rem = __builtin_fmaf(-q0, scale, x[4 * h + i]);
+                    qq = __builtin_fmaf(rem, y, q0);
+                } else {
+                    qq = __fdiv_rn(x[4 * h + i], scale);
+                }
+                q[i] = fminf(fmaxf(qq, -448.f), 448.f);
+            }
+            int v = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], v, true);
+            w[h] = (uint32_t)v;
+        }
+    }
+    return make_uint2(w[0], w[1]);
+}
+
+}  // namespace
+
+// Tokens per wave: every load of a wave's tokens is issued before the first is used, so each wave
+// keeps several rows in flight instead of one.
+constexpr int kQuantTokensPerWave = 4;
+
+__global__ __launch_bounds__(256) void quant_cache_write_kernel(QuantWriteParams p) {
+    constexpr int TPW = kQuantTokensPerWave;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * 4 + wave;
+    if (blockIdx.y == 0) {
+        // MLA rows of tokens TPW*w .. +TPW-1: lane l quantizes latent values 8l .. 8l+7 (group l / 16).
+        const int t0 = TPW * w;
+        if (t0 >= p.num_tokens) return;
+        int64_t slot[TPW];
+        float x[TPW][8], amax[TPW];
+        uint4 rope[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int t = min(t0 + i, p.num_tokens - 1);
+            slot[i] = t0 + i < p.num_tokens ? p.slots[t] : -1;
+            amax[i] = load_bf16x8(p.latent + (int64_t)t * p.latent_pitch + 16 * lane, x[i]);
+            if (lane < 8) rope[i] = *reinterpret_cast<const uint4*>(p.rope + (int64_t)t * p.rope_pitch + 16 * lane);
+        }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const float scale = __fdiv_rn(row16_max(amax[i]), 448.f);
+            const uint2 codes = quantize8(x[i], scale);
+            if (slot[i] < 0 || slot[i] >= p.num_slots) continue;  // padding token, or out of range: no write
+            const int64_t block = slot[i] / p.block_size;
+            const int64_t pos = slot[i] - block * p.block_size;
+            char* row = p.mla_dst + block * p.mla_block_stride + pos * 656;
+            *reinterpret_cast<uint2*>(row + 8 * lane) = codes;
+            if ((lane & 15) == 0) *reinterpret_cast<float*>(row + 512 + 4 * (lane >> 4)) = scale;
+            if (lane < 8) *reinterpret_cast<uint4*>(row + 528 + 16 * lane) = rope[i];
+        }
+    } else {
+        // Indexer rows of tokens 4*TPW*w .. +4*TPW-1: in step i, lane l quantizes key values 8 (l % 16)
+        // .. +7 of token 4*TPW*w + 4i + l / 16 (one token per 16-lane row).
+        const int t0 = 4 * TPW * w;
+        if (t0 >= p.num_tokens) return;  // wave-uniform
+        const int c = lane & 15;
+        int64_t slot[TPW];
+        float k[TPW][8], amax[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int tt = t0 + 4 * i + (lane >> 4);
+            const int t = min(tt, p.num_tokens - 1);
+            slot[i] = tt < p.num_tokens ? p.slots[t] : -1;
+            amax[i] = load_bf16x8(p.index_key + (int64_t)t * p.index_pitch + 16 * c, k[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const float scale = __fdiv_rn(row16_max(amax[i]), 448.f);  // every lane of the row takes part
+            const uint2 codes = quantize8(k[i], scale);
+            if (slot[i] < 0 || slot[i] >= p.num_slots) continue;
+            const int64_t block = slot[i] / p.block_size;
+            const int64_t pos = slot[i] - block * p.block_size;
+            uint32_t* row = reinterpret_cast<uint32_t*>(p.idx_dst + block * p.idx_block_stride + pos * 132);
+            row[2 * c] = codes.x;  // rows are only 4-byte aligned
+            row[2 * c + 1] = codes.y;
+            if (c == 0) row[32] = __float_as_uint(scale);
+        }
+    }
+}
+
+hipError_t launch_quant_cache_write(const QuantWriteParams& p, hipStream_t stream) {
+    if (p.num_tokens <= 0) return hipSuccess;
+    // x: work-groups of the MLA part (4 waves of kQuantTokensPerWave tokens), which is more than the
+    // indexer part needs (4 times as many tokens per wave); y: 0 = MLA rows, 1 = indexer rows.
+    const int per_wg = 4 * kQuantTokensPerWave;
+    const dim3 grid((p.num_tokens + per_wg - 1) / per_wg, p.index_key != nullptr ? 2 : 1);
+    hipLaunchKernelGGL(quant_cache_write_kernel, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {
     if (p.num_tokens <= 0) return hipSuccess;
     dim3 grid((p.num_tokens + 3) / 4, p.num_views);

@@ -26,6 +26,23 @@ struct CacheWriteParams {
 };
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
 
+// Quantize-on-write of the DSA dual cache: bf16 latent [T, 512] + RoPE [T, 64] -> 656-byte MLA rows,
+// optional bf16 indexer key [T, 128] -> 132-byte indexer rows, through one slot_mapping.
+struct QuantWriteParams {
+    const char* latent;        // row t at latent + t * latent_pitch: 512 bf16
+    const char* rope;          // 64 bf16
+    const char* index_key;     // 128 bf16, or null (MLA view only)
+    int64_t latent_pitch, rope_pitch, index_pitch;
+    const int64_t* slots;      // [num_tokens]
+    char* mla_dst;             // cache base + view offset + layer * layer_stride
+    char* idx_dst;
+    int64_t mla_block_stride, idx_block_stride;
+    int64_t num_slots;         // num_blocks * block_size
+    int32_t num_tokens;
+    int32_t block_size;
+};
+hipError_t launch_quant_cache_write(const QuantWriteParams& p, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Dense paged decode (fp16 / bf16 rows, head_dim 64 / 128 / 256; group 1, 2, 4, 8, or 2..16 at head_dim 128)
 // ---------------------------------------------------------------------------

@@ -138,3 +138,27 @@ def test_prefill_status_codes():
     need = pa.pa_prefill_workspace_bytes(good_desc(), 3, 50, 40, 2000)
     assert need == pa.pa_decode_workspace_bytes(good_desc(), 3, 2000) > 0
     assert prefill(good_desc(), max_s=2000) == E.PA_ERR_WORKSPACE
+
+
+def quant(lat=FAKE, lp=1024, rope=FAKE, rp=128, key=FAKE, kp=256, slots=FAKE, T=4, mc=FAKE, mb=8 * 100864,
+          mview=None, ic=FAKE, ib=8 * 100864, iview=None, layer=0, bs=64, nb=8):
+    mview = mview or pa.CacheView(0, 64 * 656, 100864, 656).c()
+    iview = iview or pa.CacheView(2 * 64 * 656, 64 * 132, 100864, 132).c()
+    return L._lib.pa_quantize_and_cache_mla(lat, lp, rope, rp, key, kp, slots, T, mc, mb, mview, ic, ib, iview,
+                                            layer, bs, nb, None)
+
+
+def test_quantize_write_status_codes():
+    E = L
+    assert quant(T=0) == E.PA_OK                                   # no-op, nothing enqueued
+    assert quant(T=-1) == E.PA_ERR_INVALID_ARGUMENT
+    assert quant(lat=None) == E.PA_ERR_NULL_POINTER
+    assert quant(rope=None) == E.PA_ERR_NULL_POINTER
+    assert quant(ic=None) == E.PA_ERR_NULL_POINTER                 # key given without its cache
+    assert quant(mview=pa.CacheView(0, 64 * 656, 100864, 640).c()) == E.PA_ERR_INVALID_ARGUMENT  # not 656
+    assert quant(iview=pa.CacheView(0, 64 * 132, 100864, 128).c()) == E.PA_ERR_INVALID_ARGUMENT  # not 132
+    assert quant(lp=512) == E.PA_ERR_INVALID_ARGUMENT              # pitch below one latent row
+    assert quant(lat=FAKE + 8) == E.PA_ERR_MISALIGNED
+    assert quant(mview=pa.CacheView(8, 64 * 656, 100864, 656).c()) == E.PA_ERR_MISALIGNED
+    assert quant(mb=100864 * 7) == E.PA_ERR_VIEW_OUT_OF_RANGE      # 8 blocks do not fit
+    assert quant(layer=2) == E.PA_ERR_VIEW_OUT_OF_RANGE            # layer 2 runs into the next block

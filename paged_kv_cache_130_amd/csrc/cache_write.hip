@@ -6,43 +6,93 @@
 // start + block*block_stride + position*row width. Several views (the DSA MLA and indexer
 // caches) take the same slot_mapping and land at different addresses.
 //
-// The copy is bit-exact: rows move as 16-byte or 4-byte words. One wave copies one row, so a
-// work-group of 4 waves covers 4 tokens of one view; blockIdx.y selects the view.
+// The copy is bit-exact: rows move as 16-byte or 4-byte words. A wave moves the rows of 4 tokens of
+// one view as one run of words, loading a batch of words per lane before storing any; blockIdx.y
+// selects the view.
 
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 
+namespace {
+
+constexpr int kCopyTokensPerWave = 4;  // rows of one view a wave moves
+constexpr int kCopyBatch = 4;          // words each lane loads before it stores any
+
+// A wave moves the rows of tokens TPW*w .. +TPW-1 as one flat run of words (token-major): in each
+// batch every lane loads kCopyBatch words of the run, then stores them, so a wave has up to
+// 64 * kCopyBatch words in flight whatever the row width.
+template <typename Word>
+__device__ __forceinline__ void copy_rows(const CacheWriteParams& p, int view, int t0, int lane) {
+    constexpr int TPW = kCopyTokensPerWave;
+    const int row = p.row_bytes[view];
+    const uint32_t n = (uint32_t)row / sizeof(Word);  // words per row
+    const int ntok = min(TPW, p.num_tokens - t0);
+    const uint32_t total = (uint32_t)ntok * n;
+    const char* src = p.src[view] + (int64_t)t0 * p.pitch[view];
+    const int64_t my_slot = lane < ntok ? p.slots[t0 + lane] : -1;
+
+    Word v[kCopyBatch];
+    uint32_t tok[kCopyBatch], c[kCopyBatch];
+    auto load_batch = [&](uint32_t base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u) {
+            const uint32_t j = min(base + 64 * u + lane, total - 1);  // past the end: a valid duplicate
+            tok[u] = j / n;
+            c[u] = j - tok[u] * n;
+            v[u] = reinterpret_cast<const Word*>(src + (int64_t)tok[u] * p.pitch[view])[c[u]];
+        }
+    };
+    // The first batch of source words is in flight while the slots arrive.
+    load_batch(0);
+
+    // Destination row start of each token (null for padding and out-of-range slots).
+    char* dst[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int64_t slot = (int64_t)((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)my_slot, i) |
+                                       ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_slot >> 32), i) << 32));
+        char* d = nullptr;
+        if (i < ntok && slot >= 0 && slot < p.num_slots) {
+            const int64_t block = slot / p.block_size;
+            d = p.dst[view] + block * p.block_stride[view] + (slot - block * p.block_size) * (int64_t)row;
+        }
+        dst[i] = d;
+    }
+    for (uint32_t base = 0;;) {
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u) {
+            if (base + 64 * u + lane >= total) continue;
+            char* d = dst[0];
+#pragma unroll
+            for (int i = 1; i < TPW; ++i) d = tok[u] == (uint32_t)i ? dst[i] : d;
+            if (d != nullptr) reinterpret_cast<Word*>(d)[c[u]] = v[u];
+        }
+        base += 64 * kCopyBatch;
+        if (base >= total) break;
+        load_batch(base);
+    }
+}
+
+}  // namespace
+
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
     const int view = blockIdx.y;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= p.num_tokens) return;
-    const int64_t slot = p.slots[t];
-    if (slot < 0 || slot >= p.num_slots) return;  // padding token, or out of range: no write
-    int64_t block, pos;
-    if (p.num_slots <= 0x7FFFFFFF) {
-        const uint32_t s32 = (uint32_t)slot;
-        block = s32 / (uint32_t)p.block_size;
-        pos = s32 - (uint32_t)block * (uint32_t)p.block_size;
-    } else {
-        block = slot / p.block_size;
-        pos = slot - block * p.block_size;
-    }
-    const int row = p.row_bytes[view];
-    char* dst = p.dst[view] + block * p.block_stride[view] + pos * (int64_t)row;
-    const char* src = p.src[view] + (int64_t)t * p.pitch[view];
-    if (p.vec16[view]) {
-        const int n = row >> 4;
-        for (int i = lane; i < n; i += 64)
-            reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
-    } else {
-        const int n = row >> 2;
-        for (int i = lane; i < n; i += 64)
-            reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
-    }
+    const int t0 = (blockIdx.x * 4 + wave) * kCopyTokensPerWave;
+    if (t0 >= p.num_tokens) return;
+    if (p.vec16[view]) copy_rows<uint4>(p, view, t0, lane);
+    else copy_rows<uint32_t>(p, view, t0, lane);
+}
+
+hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {
+    if (p.num_tokens <= 0) return hipSuccess;
+    const int per_wg = 4 * kCopyTokensPerWave;
+    dim3 grid((p.num_tokens + per_wg - 1) / per_wg, p.num_views);
+    hipLaunchKernelGGL(cache_write_kernel, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -206,11 +256,5 @@ hipError_t launch_quant_cache_write(const QuantWriteParams& p, hipStream_t strea
     return hipGetLastError();
 }
 
-hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {
-    if (p.num_tokens <= 0) return hipSuccess;
-    dim3 grid((p.num_tokens + 3) / 4, p.num_views);
-    hipLaunchKernelGGL(cache_write_kernel, grid, dim3(256), 0, stream, p);
-    return hipGetLastError();
-}
 
 }  // namespace pa

@@ -38,3 +38,29 @@ def reshape_and_cache(image: np.ndarray, rows: np.ndarray, slot_mapping, view: C
         a = address(view, layer, b, pos)
         out[a:a + view.row_bytes] = rows[t]
     return out
+
+
+def copy_blocks(image: np.ndarray, view: CacheView, pairs, num_layers: int, block_size: int) -> np.ndarray:
+    """Copy-on-write's data movement: for each (src, dst) block pair and each layer, the dst page takes the
+    src page's bytes.
+
+    "vLLM 技术内幕", §2.2: a sequence about to write into a block whose reference count is above 1 gets
+    a new physical block, the contents are copied, and the old block's count drops by one. The count
+    and the allocation belong to the block manager; what reaches the device is the copy. A page is
+    the block_size rows of one block in one layer of the view ("vLLM KV Cache Layout 可视化": rows of
+    a block are contiguous, pos * row_bytes apart). Every copy reads the image as it was before the
+    call; pairs whose pages overlap are a caller error (asserted here).
+    """
+    src_img = np.asarray(image, dtype=np.uint8)
+    out = np.array(src_img, copy=True)
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    dsts = pairs[:, 1]
+    assert len(np.unique(dsts)) == len(dsts), "two pairs write one block"
+    assert not set(pairs[:, 0].tolist()) & set(dsts.tolist()), "a block is both copied and overwritten"
+    page = block_size * view.row_bytes
+    for s, d in pairs:
+        for layer in range(num_layers):
+            a_s = address(view, layer, int(s), 0)
+            a_d = address(view, layer, int(d), 0)
+            out[a_d:a_d + page] = src_img[a_s:a_s + page]
+    return out

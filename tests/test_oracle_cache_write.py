@@ -54,3 +54,44 @@ def test_dual_view_write_lands_at_page_addresses():
     assert (image[547616:547616 + 656] == 0x11).all()
     assert (image[597000:597000 + 132] == 0x22).all()
     assert (image == 0x11).sum() == 656 and (image == 0x22).sum() == 132
+
+
+def test_copy_blocks_is_copy_on_write_for_a_shared_prefix():
+    # "vLLM 技术内幕" §2.2: sequences share a prefix's physical blocks (ref_cnt > 1); copy-on-write gives
+    # a sequence its own copy. After copying the shared blocks to fresh ones and pointing the
+    # sequence's table at them, every row read through the new table equals the row read through the
+    # old one, decode is unchanged, and no byte outside the destination pages moved.
+    rng = np.random.Generator(np.random.PCG64(5))
+    bs, nb, hkv, d = 16, 48, 2, 8
+    row = hkv * d * 2
+    for layout in ("layer", "block"):
+        L = 3
+        if layout == "layer":
+            view = P.CacheView(0, nb * bs * row, bs * row, row)
+            size = L * nb * bs * row
+        else:
+            view = P.CacheView(0, bs * row, L * bs * row, row)
+            size = nb * L * bs * row
+        # finite fp16 bit patterns in [0, 1), so decode outputs compare exactly
+        image = rng.integers(0, 0x3C00, size=size // 2, dtype=np.uint16).view(np.uint8)
+        shared = [3, 17, 8]                 # a 3-block prefix shared by two sequences
+        fresh = [40, 41, 42]
+        table_a = np.array(shared + [20], dtype=np.int64)
+        out = W.copy_blocks(image, view, list(zip(shared, fresh)), L, bs)
+        table_b = np.array(fresh + [20], dtype=np.int64)
+        for layer in range(L):
+            assert np.array_equal(A.gather_rows(out, view, layer, table_b, 60, bs),
+                                  A.gather_rows(image, view, layer, table_a, 60, bs))
+        moved = np.zeros(size, dtype=bool)
+        for blk in fresh:
+            for layer in range(L):
+                a = P.address(view, layer, blk, 0)
+                moved[a:a + bs * row] = True
+        assert np.array_equal(out[~moved], image[~moved])
+    # decode through either table is the same (K = V = the same rows here)
+    q = rng.integers(0, 0x3C00, size=(1, 2, d)).astype(np.uint16)
+    for tab in (table_a, table_b):
+        assert tab.shape == (4,)
+    ka = A.paged_decode(q, "f16", image, view, image, view, 1, table_a[None], [60], bs, hkv, d, 0.3)
+    kb = A.paged_decode(q, "f16", out, view, out, view, 1, table_b[None], [60], bs, hkv, d, 0.3)
+    assert np.array_equal(ka, kb)

@@ -111,3 +111,13 @@ def test_shifted_scale_group_is_caught(monkeypatch):
         return orig(np.roll(bits, 1))
     monkeypatch.setattr(Q, "quantize_group", shifted)
     _fails(TQ.test_row_layout_matches_page_byte_counts)
+
+
+def test_short_block_copy_is_caught(monkeypatch):
+    from oracle import cache_write as Wc
+
+    def short_copy(image, view, pairs, num_layers, block_size):   # the last row of each page is left behind
+        return orig(image, view, pairs, num_layers, block_size - 1)
+    orig = Wc.copy_blocks
+    monkeypatch.setattr(Wc, "copy_blocks", short_copy)
+    _fails(TW.test_copy_blocks_is_copy_on_write_for_a_shared_prefix)

@@ -154,6 +154,26 @@ def run_dense(name, steps, warmup, partition):
     dec_mean = float(np.mean(dec))
     logical, unique, write = dense_bytes(case)
     achieved = unique / (dec_mean / 1e3) / 1e9
+    cow = {}
+    if name == "gqa_prefix_copied":
+        # Copy-on-write of the shared prompt: every sequence's private prompt blocks take sequence 0's
+        # prompt pages (the copies hold the same bytes, so the workload is unchanged).
+        nprompt = case.extra["shared_prefix_blocks"]
+        bt = case.block_tables
+        pairs = np.array([[bt[0, j], bt[b, j]] for b in range(1, B) for j in range(nprompt)], dtype=np.int64)
+        pairs_d = torch.from_numpy(pairs).cuda()
+        ms = []
+        for rep in range(4):
+            a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            pa.pa_copy_blocks(pairs_d, kd, view, 1, case.block_size, case.num_blocks, v_cache=vd, v_view=view)
+            b2.record(stream)
+            torch.cuda.synchronize()
+            if rep > 0:
+                ms.append(a.elapsed_time(b2))
+        cbytes = len(pairs) * 2 * 2 * case.block_size * case.row_bytes + pairs.nbytes
+        cow = {"copy_on_write_pairs": len(pairs), "copy_on_write_ms": float(np.mean(ms)),
+               "copy_on_write_gbs": cbytes / (np.mean(ms) / 1e3) / 1e9}
     kernel = "decode_mfma_kernel" if (D == 128 and Hq // case.num_kv_heads >= 2) else "decode_dense_kernel"
     return case, {
         "workload": wdesc,
@@ -167,6 +187,7 @@ def run_dense(name, steps, warmup, partition):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(name),
                      "kernel": f"pa_decode ({kernel} + decode_reduce_kernel)", "algorithmic_bytes_per_call": unique},
         "dtype": case.dtype,
+        **cow,
         "config": {"num_seqs": B, "num_q_heads": Hq, "num_kv_heads": case.num_kv_heads, "head_dim": D,
                    "block_size": case.block_size, "num_blocks": case.num_blocks,
                    "sum_context_tokens": int(case.context_lens.sum()), "partition_size": part or "auto"},
@@ -421,6 +442,7 @@ def main():
                     "decode_tokens_per_s": r["decode_tokens_per_s"], "decode_call_ms": r["decode_call_ms"],
                     "decode_call_ms_p10_p90": r["decode_call_ms_p10_p90"],
                     "decode_kv_gbs_logical": r["decode_kv_gbs_logical"], "roofline": r["roofline"]})
+        res.update({k: r[k] for k in ("copy_on_write_pairs", "copy_on_write_ms", "copy_on_write_gbs") if k in r})
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = cpu_baseline(case)
         del case
@@ -441,6 +463,9 @@ def main():
             extra[name] = {"workload": r["workload"], "decode_call_ms": r["decode_call_ms"],
                            "kv_gbs": r["roofline"]["achieved"], "frac_of_hbm_peak": r["roofline"]["frac"],
                            "kv_gbs_logical": r["decode_kv_gbs_logical"], "decode_tokens_per_s": r["decode_tokens_per_s"]}
+            for k in ("copy_on_write_pairs", "copy_on_write_ms", "copy_on_write_gbs"):
+                if k in r:
+                    extra[name][k] = r[k]
             del case
             torch.cuda.empty_cache()
         extra["long_mixed"] = run_mixed(10, 3)

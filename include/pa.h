@@ -181,6 +181,26 @@ int32_t pa_quantize_and_cache_mla(const void* latent, int64_t latent_pitch, cons
                                   pa_cache_view index_view, int32_t layer, int32_t block_size,
                                   int64_t num_blocks, void* stream);
 
+/* pa_copy_blocks: the data movement of copy-on-write (and of any block move inside a pool).
+ *
+ * [INSIDE] §2.2: physical blocks carry a reference count; a sequence about to write into a block
+ * shared with others (count above 1) gets a new physical block, the contents are copied, and the old
+ * block's count drops by one. The counting and allocation are the caller's; this call does the
+ * copy: for each pair (src, dst) and each layer l < num_layers, the page of dst (block_size rows
+ * starting at offset + l*layer_stride + dst*block_stride) takes the bytes of src's page, in the K
+ * view and, if v_cache is not NULL, the V view.
+ *
+ *   block_pairs    device int64 [num_pairs, 2]: (src, dst) physical block ids. A pair with an id
+ *                  outside [0, num_blocks) is skipped. No block may be the dst of two pairs or both a
+ *                  src and a dst in one call (caller error: the result is then unspecified).
+ *   k_cache, v_cache, *_bytes, *_view  as for pa_reshape_and_cache; every layer < num_layers of
+ *                  each view must lie inside its allocation.
+ * Alignment: bases, view offsets and strides 4 bytes (16 bytes selects 16-byte copies).
+ * num_pairs == 0 or num_layers == 0 is a no-op. */
+int32_t pa_copy_blocks(void* k_cache, int64_t k_cache_bytes, pa_cache_view k_view, void* v_cache,
+                       int64_t v_cache_bytes, pa_cache_view v_view, const int64_t* block_pairs, int32_t num_pairs,
+                       int32_t num_layers, int32_t block_size, int64_t num_blocks, void* stream);
+
 /* Workspace bytes pa_decode needs for this shape (0 when no split-context partials are needed). */
 size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t max_context_len);
 

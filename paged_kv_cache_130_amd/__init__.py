@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     abi_version,
     dense_desc,
     dense_view,
+    pa_copy_blocks,
     pa_decode,
     pa_decode_workspace_bytes,
     pa_prefill_chunk,

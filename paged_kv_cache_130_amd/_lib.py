@@ -29,6 +29,7 @@ PA_KV_BF16 = 1
 PA_KV_MLA656_E4M3 = 2
 
 EXPORTS = ("pa_abi_version", "pa_status_string", "pa_last_hip_error", "pa_reshape_and_cache", "pa_quantize_and_cache_mla",
+           "pa_copy_blocks",
            "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_workspace_bytes", "pa_prefill_chunk")
 
 
@@ -72,6 +73,7 @@ def _load():
         "pa_reshape_and_cache": (I32, [P, I64, P, I64, P, I32, P, I64, V, P, I64, V, I32, I32, I64, P]),
         "pa_quantize_and_cache_mla": (I32, [P, I64, P, I64, P, I64, P, I32, P, I64, V, P, I64, V, I32, I32, I64,
                                             P]),
+        "pa_copy_blocks": (I32, [P, I64, V, P, I64, V, P, I32, I32, I32, I64, P]),
         "pa_decode_workspace_bytes": (SZ, [ctypes.POINTER(pa_attn_desc), I32, I32]),
         "pa_decode": (I32, [P, P, P, P, P, I32, P, I32, I32, ctypes.c_float, ctypes.POINTER(pa_attn_desc), P, SZ,
                             P]),
@@ -226,6 +228,20 @@ def pa_quantize_and_cache_mla(latent, rope, slot_mapping, mla_cache, mla_view: C
                                         _nbytes(index_cache) if index_cache is not None else 0, iv, layer,
                                         block_size, num_blocks, _stream(stream))
     _check("pa_quantize_and_cache_mla", st)
+
+
+def pa_copy_blocks(block_pairs, k_cache, k_view: CacheView, num_layers: int, block_size: int, num_blocks: int,
+                   v_cache=None, v_view: CacheView | None = None, stream=None):
+    """Copy each (src, dst) block pair's pages (all num_layers layers) in the K (and V) view."""
+    _require_device(block_pairs, k_cache, v_cache)
+    if block_pairs.dtype.itemsize != 8 or not block_pairs.is_contiguous() or block_pairs.dim() != 2 \
+            or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be a contiguous int64 [n, 2] tensor")
+    vv = v_view.c() if v_view is not None else pa_cache_view(0, 0, 0, 0, 0)
+    st = _lib.pa_copy_blocks(_ptr(k_cache), _nbytes(k_cache), k_view.c(), _ptr(v_cache),
+                             _nbytes(v_cache) if v_cache is not None else 0, vv, _ptr(block_pairs),
+                             block_pairs.shape[0], num_layers, block_size, num_blocks, _stream(stream))
+    _check("pa_copy_blocks", st)
 
 
 def pa_decode_workspace_bytes(desc: AttnDesc, num_seqs: int, max_context_len: int) -> int:

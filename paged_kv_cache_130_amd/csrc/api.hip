@@ -273,6 +273,41 @@ int32_t pa_quantize_and_cache_mla(const void* latent, int64_t latent_pitch, cons
     return hip_status(pa::launch_quant_cache_write(p, static_cast<hipStream_t>(stream)));
 }
 
+int32_t pa_copy_blocks(void* k_cache, int64_t k_cache_bytes, pa_cache_view k_view, void* v_cache,
+                       int64_t v_cache_bytes, pa_cache_view v_view, const int64_t* block_pairs, int32_t num_pairs,
+                       int32_t num_layers, int32_t block_size, int64_t num_blocks, void* stream) {
+    if (num_pairs < 0 || num_layers < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_pairs == 0 || num_layers == 0) return PA_OK;
+    if (!k_cache || !block_pairs) return PA_ERR_NULL_POINTER;
+    if (block_size <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)num_pairs * num_layers > 0x7FFFFFFFLL) return PA_ERR_UNSUPPORTED;
+    if (!aligned(block_pairs, 8)) return PA_ERR_MISALIGNED;
+    void* base[2] = {k_cache, v_cache};
+    const int64_t bytes[2] = {k_cache_bytes, v_cache_bytes};
+    const pa_cache_view* view[2] = {&k_view, &v_view};
+    const int nviews = v_cache ? 2 : 1;
+    pa::BlockCopyParams p;
+    std::memset(&p, 0, sizeof(p));
+    for (int i = 0; i < nviews; ++i) {
+        // The last layer's pages must lie inside the allocation.
+        int32_t st = check_view(*view[i], num_layers - 1, num_blocks, block_size, bytes[i]);
+        if (st != PA_OK) return st;
+        if (!aligned(base[i], 4) || !view_aligned(*view[i], 0, 4) || !aligned(view[i]->layer_stride, 4))
+            return PA_ERR_MISALIGNED;
+        p.base[i] = static_cast<char*>(base[i]) + view[i]->offset;
+        p.layer_stride[i] = view[i]->layer_stride;
+        p.block_stride[i] = view[i]->block_stride;
+        p.page_bytes[i] = (int64_t)block_size * view[i]->row_bytes;
+        p.vec16[i] = aligned(base[i], 16) && view_aligned(*view[i], 0, 16) && aligned(view[i]->layer_stride, 16);
+    }
+    p.pairs = block_pairs;
+    p.num_blocks = num_blocks;
+    p.num_pairs = num_pairs;
+    p.num_layers = num_layers;
+    p.num_views = nviews;
+    return hip_status(pa::launch_block_copy(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t max_context_len) {
     if (!desc || num_seqs <= 0 || max_context_len <= 0) return 0;
     if (desc->kv_format == PA_KV_F16 || desc->kv_format == PA_KV_BF16) {

@@ -257,4 +257,54 @@ hipError_t launch_quant_cache_write(const QuantWriteParams& p, hipStream_t strea
 }
 
 
+// ---------------------------------------------------------------------------
+// Block copy for copy-on-write.
+//
+// "vLLM 技术内幕" §2.2: a sequence about to write into a block whose reference count is above 1 gets
+// a new physical block and the contents are copied; the count and the allocation are the block
+// manager's. Here is the copy: one work-group per (pair, layer) and view moves the page (block_size
+// rows, contiguous in every view of "vLLM KV Cache Layout 可视化") in batches of 4 words per thread.
+// Block ids outside [0, num_blocks) skip the pair.
+// ---------------------------------------------------------------------------
+
+template <typename Word>
+__device__ __forceinline__ void copy_page(const char* src, char* dst, int64_t bytes) {
+    constexpr int U = 4;
+    const int64_t n = bytes / (int64_t)sizeof(Word);
+    const Word* s = reinterpret_cast<const Word*>(src);
+    Word* d = reinterpret_cast<Word*>(dst);
+    for (int64_t base = 0; base < n; base += 256 * U) {
+        Word v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + 256 * u + threadIdx.x;
+            if (i < n) v[u] = s[i];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + 256 * u + threadIdx.x;
+            if (i < n) d[i] = v[u];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void block_copy_kernel(BlockCopyParams p) {
+    const int view = blockIdx.y;
+    const int pair = blockIdx.x / p.num_layers;
+    const int layer = blockIdx.x - pair * p.num_layers;
+    const int64_t src = p.pairs[2 * pair], dst = p.pairs[2 * pair + 1];
+    if (src < 0 || src >= p.num_blocks || dst < 0 || dst >= p.num_blocks) return;
+    const char* s = p.base[view] + layer * p.layer_stride[view] + src * p.block_stride[view];
+    char* d = p.base[view] + layer * p.layer_stride[view] + dst * p.block_stride[view];
+    if (p.vec16[view]) copy_page<uint4>(s, d, p.page_bytes[view]);
+    else copy_page<uint32_t>(s, d, p.page_bytes[view]);
+}
+
+hipError_t launch_block_copy(const BlockCopyParams& p, hipStream_t stream) {
+    if (p.num_pairs <= 0 || p.num_layers <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((int64_t)p.num_pairs * p.num_layers), p.num_views);
+    hipLaunchKernelGGL(block_copy_kernel, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace pa

@@ -43,6 +43,19 @@ struct QuantWriteParams {
 };
 hipError_t launch_quant_cache_write(const QuantWriteParams& p, hipStream_t stream);
 
+// Copy-on-write's data movement: for each (src, dst) block pair and each layer, copy the page
+// (block_size contiguous rows) of every view.
+struct BlockCopyParams {
+    char* base[2];             // cache base + view offset (layer 0)
+    int64_t layer_stride[2], block_stride[2];
+    int64_t page_bytes[2];     // block_size * row_bytes
+    int32_t vec16[2];          // 1: every address of the view is 16-byte aligned
+    const int64_t* pairs;      // [num_pairs, 2]: src block, dst block
+    int64_t num_blocks;
+    int32_t num_pairs, num_layers, num_views;
+};
+hipError_t launch_block_copy(const BlockCopyParams& p, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Dense paged decode (fp16 / bf16 rows, head_dim 64 / 128 / 256; group 1, 2, 4, 8, or 2..16 at head_dim 128)
 // ---------------------------------------------------------------------------

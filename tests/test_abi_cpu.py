@@ -162,3 +162,23 @@ def test_quantize_write_status_codes():
     assert quant(mview=pa.CacheView(8, 64 * 656, 100864, 656).c()) == E.PA_ERR_MISALIGNED
     assert quant(mb=100864 * 7) == E.PA_ERR_VIEW_OUT_OF_RANGE      # 8 blocks do not fit
     assert quant(layer=2) == E.PA_ERR_VIEW_OUT_OF_RANGE            # layer 2 runs into the next block
+
+
+def copyb(k=FAKE, kb=3 * 64 * 16 * 2048, kview=None, v=FAKE, vb=3 * 64 * 16 * 2048, vview=None, pairs=FAKE, n=4,
+          layers=3, bs=16, nb=64):
+    kview = kview or pa.CacheView(0, 64 * 16 * 2048, 16 * 2048, 2048).c()
+    vview = vview or pa.CacheView(0, 64 * 16 * 2048, 16 * 2048, 2048).c()
+    return L._lib.pa_copy_blocks(k, kb, kview, v, vb, vview, pairs, n, layers, bs, nb, None)
+
+
+def test_copy_blocks_status_codes():
+    E = L
+    assert copyb(n=0) == E.PA_OK and copyb(layers=0) == E.PA_OK    # no-ops
+    assert copyb(n=-1) == E.PA_ERR_INVALID_ARGUMENT
+    assert copyb(k=None) == E.PA_ERR_NULL_POINTER
+    assert copyb(pairs=None) == E.PA_ERR_NULL_POINTER
+    assert copyb(layers=4) == E.PA_ERR_VIEW_OUT_OF_RANGE            # a 4th layer does not fit
+    assert copyb(vb=2 * 64 * 16 * 2048) == E.PA_ERR_VIEW_OUT_OF_RANGE
+    assert copyb(pairs=FAKE + 4) == E.PA_ERR_MISALIGNED
+    assert copyb(kview=pa.CacheView(2, 64 * 16 * 2048, 16 * 2048, 2048).c(), kb=3 * 64 * 16 * 2048 + 16) == \
+        E.PA_ERR_MISALIGNED

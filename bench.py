@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TF = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = ("api.hip", "cache_write.hip", "decode_dense.hip", "decode_mfma.hip", "decode_mla.hip",
-                  "prefill_mfma.hip", "decode_common.h", "mfma_common.h", "pa_device.h", "pa_internal.h")
+                  "prefill_mfma.hip", "decode_common.h", "decode_mfma.h", "mfma_common.h", "pa_device.h", "pa_internal.h")
 
 
 def kernel_source_hash() -> str:

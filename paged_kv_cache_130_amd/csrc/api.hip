@@ -483,8 +483,6 @@ int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const vo
     dp.is_bf16 = d.kv_format == PA_KV_BF16;
     dp.head_dim = d.qk_dim;
     dp.group = d.num_q_heads / d.num_kv_heads;
-    st = hip_status(pa::launch_decode_dense(dp, static_cast<hipStream_t>(stream)));
-    if (st != PA_OK) return st;
 
     // 2) Chunk rows (query length >= 2): causal attention over the paged context.
     pa::PrefillParams pp;
@@ -514,8 +512,12 @@ int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const vo
     pp.group = dp.group;
     pp.rows_per_item = 128;
     pp.total_q = total_q;
-    if (max_query_len < 2) return PA_OK;
-    return hip_status(pa::launch_prefill_chunk(pp, static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // Grouped heads at head_dim 128 decode on the matrix cores: one launch takes both kinds of rows.
+    if (max_query_len >= 2 && d.qk_dim == 128 && dp.group >= 2) return hip_status(pa::launch_mixed_chunk(pp, dp, s));
+    st = hip_status(pa::launch_decode_dense(dp, s));
+    if (st != PA_OK || max_query_len < 2) return st;
+    return hip_status(pa::launch_prefill_chunk(pp, s));
 }
 
 }  // extern "C"

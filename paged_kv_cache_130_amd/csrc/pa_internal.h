@@ -153,5 +153,8 @@ struct PrefillParams {
     int32_t total_q;           // query rows of the call (bounds the grid)
 };
 hipError_t launch_prefill_chunk(const PrefillParams& p, hipStream_t stream);
+// Chunk rows and the decode rows of the same call in one launch (decode rows on the grouped-query
+// matrix-core decode: head_dim 128, group 2..16), then the decode rows' partition merge.
+hipError_t launch_mixed_chunk(const PrefillParams& pp, const DenseDecodeParams& dp, hipStream_t stream);
 
 }  // namespace pa

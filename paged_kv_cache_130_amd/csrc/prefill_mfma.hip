@@ -19,7 +19,10 @@
 // probabilities go in as hi + lo pairs (pack2_split). Sequences with a single query row are not
 // handled here: they are the decode rows of the call and go through the split-context decode.
 
+#include <algorithm>
+
 #include "decode_common.h"
+#include "decode_mfma.h"
 #include "mfma_common.h"
 
 namespace pa {
@@ -97,14 +100,14 @@ __device__ __forceinline__ char* pv_stage() {
 // rows of a transposed value read get different chunks.
 __device__ __forceinline__ int pswz(int r) { return (((r >> 2) & 3) << 1) | (r & 1); }
 
+// One work-group's item of the chunk rows (item = (sequence, row block) index * Hkv + K/V head).
 template <bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(PrefillParams p) {
+__device__ __forceinline__ void prefill_block(const PrefillParams& p, const int item) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4;
     const int c = lane & 15;
 
-    const int item = blockIdx.x;
     const int kvh = item % p.num_kv_heads;
     int s, rb;
     if (!find_chunk_work(item / p.num_kv_heads, p, s, rb)) return;  // the same for the whole work-group
@@ -404,18 +407,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-hipError_t launch_prefill_chunk(const PrefillParams& p, hipStream_t stream) {
-    if (p.num_seqs <= 0) return hipSuccess;
-    // Upper bound of the work-groups: every sequence's rows rounded up to whole row blocks.
+template <bool BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(PrefillParams p) {
+    prefill_block<BF16>(p, blockIdx.x);
+}
+
+// A mixed call in one launch: some work-groups take the chunk rows, the others the decode rows on the
+// grouped-query decode waves. The chunk rows are bound by the matrix cores and the decode rows by
+// HBM, so running them side by side hides part of the shorter behind the longer. The two kinds
+// alternate in dispatch order while both last (even = chunk rows, odd = decode rows); of the orders
+// measured (chunk rows first, alternating singly, alternating in runs of 8), this one gives the
+// shortest call when the chunk rows alone fill every CU, and the same total over both steps of a
+// chunked prompt. Both kinds fit the same budget: two waves per SIMD, and the chunk rows' LDS tiles
+// limit a CU to two work-groups, which is also the decode waves' register-limited occupancy.
+template <bool BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mixed_chunk_kernel(
+    PrefillParams pp, DenseDecodeParams dp, int prefill_wgs, int decode_wgs) {
+    const int both = min(prefill_wgs, decode_wgs);
+    int b = blockIdx.x;
+    bool chunk;
+    if (b < 2 * both) {
+        chunk = (b & 1) == 0;
+        b >>= 1;
+    } else {
+        b -= 2 * both;
+        chunk = b < prefill_wgs - both;
+        b = both + (chunk ? b : b - (prefill_wgs - both));
+    }
+    if (chunk) {
+        prefill_block<BF16>(pp, b);
+    } else {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        decode_mfma_wave<BF16>(dp, b * 4 + wave);
+    }
+}
+
+namespace {
+
+// Upper bound of the chunk-row work-groups: every sequence's rows rounded up to whole row blocks.
+int64_t prefill_wgs(const PrefillParams& p) {
     const int64_t per_seq = ((int64_t)p.max_query_len * p.group + p.rows_per_item - 1) / p.rows_per_item;
     const int64_t bound = ((int64_t)p.total_q * p.group + p.rows_per_item - 1) / p.rows_per_item + p.num_seqs;
-    const int64_t wgs = min(per_seq * p.num_seqs, bound) * p.num_kv_heads;
+    return std::max<int64_t>(0, std::min(per_seq * p.num_seqs, bound) * p.num_kv_heads);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_chunk(const PrefillParams& p, hipStream_t stream) {
+    if (p.num_seqs <= 0) return hipSuccess;
+    const int64_t wgs = prefill_wgs(p);
     if (wgs <= 0) return hipSuccess;
     if (p.is_bf16)
         hipLaunchKernelGGL((prefill_mfma_kernel<true>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     else
         hipLaunchKernelGGL((prefill_mfma_kernel<false>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     return hipGetLastError();
+}
+
+hipError_t launch_mixed_chunk(const PrefillParams& pp, const DenseDecodeParams& dp, hipStream_t stream) {
+    const int64_t pw = pp.num_seqs > 0 ? prefill_wgs(pp) : 0;
+    const int64_t dw = ((int64_t)dp.num_kv_heads * dp.num_seqs * dp.max_parts + 3) / 4;
+    if (pw + dw <= 0) return hipSuccess;
+    if (pw + dw > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (pp.is_bf16)
+        hipLaunchKernelGGL((mixed_chunk_kernel<true>), dim3((unsigned)(pw + dw)), dim3(256), 0, stream, pp, dp, (int)pw,
+                           (int)dw);
+    else
+        hipLaunchKernelGGL((mixed_chunk_kernel<false>), dim3((unsigned)(pw + dw)), dim3(256), 0, stream, pp, dp,
+                           (int)pw, (int)dw);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || dp.max_parts <= 1) return e;
+    return launch_decode_reduce(dp, stream);
 }
 
 }  // namespace pa

@@ -33,6 +33,10 @@ Readings where the pages are silent:
   RoPE values; little-endian.
 * MLA scores use [latent | rope] (576 dims). The value is the dequantized
   512-dim latent only.
+* FP8 dense caches ("deep dive into vLLM 05" §3.4: quantize on write,
+  dequantize on read, FP8 the safest format): one OCP E4M3 byte per value and
+  one float32 scale per cache (K and V each); the value is code * scale. The
+  query and output stay bf16.
 """
 
 from __future__ import annotations
@@ -61,8 +65,15 @@ def gather_rows(image: np.ndarray, view: CacheView, layer: int, table_row, num_t
     return out
 
 
-def dense_heads(rows: np.ndarray, dtype: str, num_kv_heads: int, head_dim: int) -> np.ndarray:
-    """Decode dense NHD rows ([n, Hkv*D] 16-bit values) into float64 [n, Hkv, D]."""
+def dense_heads(rows: np.ndarray, dtype: str, num_kv_heads: int, head_dim: int, scale: float = 1.0) -> np.ndarray:
+    """Decode dense NHD rows into float64 [n, Hkv, D].
+
+    dtype "f16" / "bf16": 16-bit values. dtype "e4m3": one OCP E4M3 byte per value, times the cache's
+    float32 ``scale`` (dequantize-on-read, "deep dive into vLLM 05" §3.4).
+    """
+    if dtype == "e4m3":
+        codes = rows[:, :num_kv_heads * head_dim]
+        return (e4m3_bytes_to_f64(codes) * float(scale)).reshape(len(rows), num_kv_heads, head_dim)
     words = u16le_bytes(rows[:, :num_kv_heads * head_dim * 2])
     return bits_to_f64(words, dtype).reshape(len(rows), num_kv_heads, head_dim)
 
@@ -82,12 +93,16 @@ def softmax_attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) ->
 
 def paged_decode(q_bits, dtype: str, k_image: np.ndarray, k_view: CacheView, v_image: np.ndarray,
                  v_view: CacheView, layer: int, block_tables, context_lens, block_size: int,
-                 num_kv_heads: int, head_dim: int, scale: float, select=None) -> np.ndarray:
-    """Paged decode. q [B, Hq, D] stored bits. Returns float64 [B, Hq, D].
+                 num_kv_heads: int, head_dim: int, scale: float, select=None, kv_dtype: str | None = None,
+                 k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """Paged decode. q [B, Hq, D] stored bits of type ``dtype``. Returns float64 [B, Hq, D].
 
     ``select`` is an optional list of (seq, q_head) pairs; only those outputs
-    are computed and the rest are NaN.
+    are computed and the rest are NaN. ``kv_dtype`` (default: ``dtype``) is the
+    cache's type; for "e4m3" the K and V values are the codes times ``k_scale``
+    and ``v_scale``.
     """
+    kv_dtype = kv_dtype or dtype
     q = bits_to_f64(q_bits, dtype)
     B, Hq, D = q.shape
     g = Hq // num_kv_heads
@@ -97,10 +112,10 @@ def paged_decode(q_bits, dtype: str, k_image: np.ndarray, k_view: CacheView, v_i
         want.setdefault(int(b), []).append(int(h))
     for b, heads in want.items():
         n = int(context_lens[b])
-        K = dense_heads(gather_rows(k_image, k_view, layer, block_tables[b], n, block_size), dtype,
-                        num_kv_heads, head_dim)
-        V = dense_heads(gather_rows(v_image, v_view, layer, block_tables[b], n, block_size), dtype,
-                        num_kv_heads, head_dim)
+        K = dense_heads(gather_rows(k_image, k_view, layer, block_tables[b], n, block_size), kv_dtype,
+                        num_kv_heads, head_dim, k_scale)
+        V = dense_heads(gather_rows(v_image, v_view, layer, block_tables[b], n, block_size), kv_dtype,
+                        num_kv_heads, head_dim, v_scale)
         for h in heads:
             kvh = h // g
             out[b, h] = softmax_attend(q[b, h], K[:, kvh, :], V[:, kvh, :], scale)

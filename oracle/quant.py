@@ -122,3 +122,16 @@ def quantize_and_cache(image: np.ndarray, latent_bits, rope_bits, index_bits, sl
             np.zeros((0, 132), dtype=np.uint8)
         out = reshape_and_cache(out, idx_rows, slot_mapping, index_view, layer, block_size)
     return out
+
+
+def dense_fp8_rows(src_bits, src_dtype: str, scale) -> np.ndarray:
+    """Dense rows for an FP8 cache: 16-bit values [n, m] (stored bits) -> E4M3 codes [n, m].
+
+    Reading for the dense FP8 cache ("deep dive into vLLM 05" §3.4 names quantize-on-write and FP8; the
+    granularity is left open): one float32 scale per cache, given by the caller; each value is stored
+    as the E4M3 code nearest to the float32 quotient x / scale, saturating at 448.
+    """
+    from .numerics import bits_to_f64
+    x = bits_to_f64(np.asarray(src_bits, dtype=np.uint16), src_dtype).astype(np.float32)  # exact
+    q = (x / np.float32(scale)).astype(np.float32)                                      # float32 division
+    return e4m3_encode(q.astype(np.float64))

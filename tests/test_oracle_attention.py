@@ -280,3 +280,34 @@ def test_mla_with_unit_scales_and_zero_rope_is_mqa_decode():
     ref = A.paged_decode(np.ascontiguousarray(q[:, :, :512]), "bf16", img(pool), dv, img(pool), dv, 0, tables,
                          ctx, bs, 1, 512, 0.05)
     np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_fp8_cache_decode_equals_bf16_decode_of_the_dequantized_values():
+    # With scales that are powers of two, code * scale is exactly representable in bf16 (E4M3 values
+    # carry 4 significant bits). So an FP8 cache and a bf16 cache holding the dequantized values must
+    # give the same float64 decode: this pins the FP8 read path (codes, scales, and where each scale
+    # applies) against the plain dense path.
+    from oracle import numerics as N
+    import torch
+    rng = np.random.Generator(np.random.PCG64(17))
+    bs, nb, hkv, hq, d = 16, 24, 2, 4, 64
+    row8, row16 = hkv * d, hkv * d * 2
+    k_codes = rng.integers(0, 256, size=nb * bs * row8, dtype=np.uint8)
+    v_codes = rng.integers(0, 256, size=nb * bs * row8, dtype=np.uint8)
+    for c in (k_codes, v_codes):
+        c[(c & 0x7F) == 0x7F] = 0x3C          # no NaN codes
+    ks, vs = 2.0 ** -3, 2.0 ** 2
+    to_bf16 = lambda codes, s: torch.from_numpy(N.e4m3_bytes_to_f64(codes) * s).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint8)
+    k16, v16 = to_bf16(k_codes, ks), to_bf16(v_codes, vs)
+    assert np.array_equal(N.bf16_bits_to_f64(k16.view(np.uint16)), N.e4m3_bytes_to_f64(k_codes) * ks)
+    view8 = P.CacheView(0, 0, bs * row8, row8)
+    view16 = P.CacheView(0, 0, bs * row16, row16)
+    tables = rng.permutation(nb).reshape(3, 8).astype(np.int64)
+    ctx = [1, 50, 128]
+    q = torch.randn(3, hq, d, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+    a = A.paged_decode(q, "bf16", k_codes, view8, v_codes, view8, 0, tables, ctx, bs, hkv, d, 0.125,
+                       kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    b = A.paged_decode(q, "bf16", k16, view16, v16, view16, 0, tables, ctx, bs, hkv, d, 0.125)
+    assert np.array_equal(a, b)

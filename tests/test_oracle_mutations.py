@@ -121,3 +121,12 @@ def test_short_block_copy_is_caught(monkeypatch):
     orig = Wc.copy_blocks
     monkeypatch.setattr(Wc, "copy_blocks", short_copy)
     _fails(TW.test_copy_blocks_is_copy_on_write_for_a_shared_prefix)
+
+
+def test_swapped_fp8_scales_are_caught(monkeypatch):
+    orig = A.paged_decode
+
+    def swapped(*args, k_scale=1.0, v_scale=1.0, **kw):
+        return orig(*args, k_scale=v_scale, v_scale=k_scale, **kw)
+    monkeypatch.setattr(A, "paged_decode", swapped)
+    _fails(TA.test_fp8_cache_decode_equals_bf16_decode_of_the_dequantized_values)

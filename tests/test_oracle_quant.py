@@ -162,3 +162,19 @@ def test_quantize_and_cache_scatters_like_reshape_and_cache():
     assert (got[~touched] == 0xA5).all()
     only_mla = Q.quantize_and_cache(image, lat, rope, None, slots, mla_v, None, 1, bs)
     assert np.array_equal(only_mla, reshape_and_cache(image, rows, slots, mla_v, 1, bs))
+
+
+@pytest.mark.parametrize("src", ["bf16", "f16"])
+def test_dense_fp8_rows_match_torch(src):
+    # The dense recipe with a per-cache scale, written with torch float32 operations: x / scale, clamped
+    # to the format's range (the reading saturates), cast to float8_e4m3fn.
+    g = torch.Generator().manual_seed(13)
+    x = torch.randn(64, 256, generator=g) * 3
+    x[0, :8] = torch.tensor([1e4, -1e4, 500.0, -470.0, 0.0, -0.0, 1e-6, -1e-6])   # saturating, zero, tiny
+    tdt = torch.bfloat16 if src == "bf16" else torch.float16
+    bits = x.to(tdt).view(torch.int16).numpy().view(np.uint16)
+    scale = np.float32(0.0625)
+    got = Q.dense_fp8_rows(bits, src, scale)
+    xf = torch.from_numpy(bits.astype(np.int16)).view(tdt).to(torch.float32)
+    ref = (xf / torch.tensor(scale)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)

@@ -28,9 +28,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E peak, GB/s
+FP8_SCALE = 2.0 ** -5       # K and V scale of the FP8 cache variants (N(0,1) values use codes up to ~160)
 MFMA_BF16_PEAK_TF = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
-KERNEL_SOURCES = ("api.hip", "cache_write.hip", "decode_dense.hip", "decode_mfma.hip", "decode_mla.hip",
+KERNEL_SOURCES = ("api.hip", "cache_write.hip", "decode_dense.hip", "decode_fp8.hip", "decode_mfma.hip", "decode_mla.hip",
                   "prefill_mfma.hip", "decode_common.h", "decode_mfma.h", "mfma_common.h", "pa_device.h", "pa_internal.h")
 
 
@@ -48,7 +49,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mha13b",
-                    choices=["mha13b", "gqa_prefix", "gqa_prefix_copied", "long_decode", "long_mixed", "dsa_mla"])
+                    choices=["mha13b", "gqa_prefix", "gqa_prefix_copied", "long_decode", "long_mixed", "dsa_mla",
+                             "mha13b_fp8", "gqa_prefix_copied_fp8"])
     ap.add_argument("--partition", type=int, default=0, help="pa_decode partition_size (0: library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the short runs of the other workloads")
@@ -98,11 +100,11 @@ def dense_case(name):
         "long-context decode: 8 seqs x 32768 tokens, 32/8 heads x 128, bf16, bs 16, partitions of 512")
 
 
-def dense_bytes(case):
+def dense_bytes(case, row=None):
     """Algorithmic bytes: distinct K/V rows read once, Q, output, table entries, lengths; and the step's write."""
     import numpy as np
     ctx = case.context_lens.astype(np.int64)
-    row = case.row_bytes
+    row = row or case.row_bytes
     B, Hq = case.num_seqs, case.num_q_heads
     if case.extra.get("shared_prefix_blocks") and not case.extra.get("copied_prefix"):
         unique_tokens = int(ctx.sum() - (B - 1) * case.extra["shared_prefix_blocks"] * case.block_size)
@@ -117,13 +119,52 @@ def run_dense(name, steps, warmup, partition):
     import numpy as np
     import torch
     import paged_kv_cache_130_amd as pa
-    case, wdesc = dense_case(name)
+    fp8 = name.endswith("_fp8")
+    case, wdesc = dense_case(name[:-4] if fp8 else name)
     B, Hq, D = case.num_seqs, case.num_q_heads, case.head_dim
     kd, vd = case.k_pool, case.v_pool
     view = pa.dense_view(case.block_size, case.num_kv_heads, D)
     part = partition or (512 if name == "long_decode" else 0)
     desc = pa.dense_desc(case.dtype, Hq, case.num_kv_heads, D, case.block_size, case.num_blocks, kd.numel() * 2,
                          vd.numel() * 2, part)
+    row8 = None
+    quant = {}
+    if fp8:
+        # The same workload with its K/V cache in FP8 (E4M3, one scale per cache): the 16-bit pools are
+        # quantized on the device through pa_quantize_and_cache (every slot), queries become bf16.
+        nb, bs, hkv = case.num_blocks, case.block_size, case.num_kv_heads
+        tdt = torch.float16 if case.dtype == "f16" else torch.bfloat16
+        row8 = hkv * D
+        view8 = pa.dense_view(bs, hkv, D, 1)
+        k8 = torch.empty((nb, bs, hkv, D), dtype=torch.uint8, device="cuda")
+        v8 = torch.empty_like(k8)
+        all_slots = torch.arange(nb * bs, dtype=torch.int64, device="cuda")
+        ksrc = torch.nan_to_num(kd.view(tdt), nan=0.0).reshape(nb * bs, row8)
+        vsrc = torch.nan_to_num(vd.view(tdt), nan=0.0).reshape(nb * bs, row8)
+        qms = []
+        for rep in range(3):
+            a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            pa.pa_quantize_and_cache(ksrc, all_slots, k8, view8, 0, bs, nb, FP8_SCALE,
+                                     src_dtype="f16" if case.dtype == "f16" else "bf16", v=vsrc, v_cache=v8,
+                                     v_view=view8, v_scale=FP8_SCALE)
+            b2.record()
+            torch.cuda.synchronize()
+            if rep > 0:
+                qms.append(a.elapsed_time(b2))
+        qbytes = 2 * nb * bs * row8 * 3 + nb * bs * 8
+        quant = {"quantize_pool_ms": float(np.mean(qms)), "quantize_pool_gbs": qbytes / (np.mean(qms) / 1e3) / 1e9}
+        del ksrc, vsrc
+        case.k_pool = case.v_pool = None
+        kd, vd = k8, v8
+        torch.cuda.empty_cache()
+        case.q = case.q.view(tdt).to(torch.bfloat16).view(torch.int16)
+        new_k = case.new_k.view(tdt).to(torch.bfloat16).reshape(B, row8)
+        new_v = case.new_v.view(tdt).to(torch.bfloat16).reshape(B, row8)
+        view = view8
+        desc = pa.dense_desc("fp8", Hq, hkv, D, bs, nb, k8.numel(), v8.numel(), part, k_scale=FP8_SCALE,
+                             v_scale=FP8_SCALE)
+        wdesc += "; K/V cache in FP8 E4M3 (one scale per cache), bf16 queries"
     max_ctx = int(case.context_lens.max())
     ws = torch.empty(max(16, pa.pa_decode_workspace_bytes(desc, B, max_ctx)), dtype=torch.uint8, device="cuda")
     out = torch.empty(B, Hq, D, dtype=torch.int16, device="cuda")
@@ -133,8 +174,12 @@ def run_dense(name, steps, warmup, partition):
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        pa.pa_reshape_and_cache(case.new_k, slots, kd, view, 0, case.block_size, case.num_blocks, v=case.new_v,
-                                v_cache=vd, v_view=view)
+        if fp8:
+            pa.pa_quantize_and_cache(new_k, slots, kd, view, 0, case.block_size, case.num_blocks, FP8_SCALE, v=new_v,
+                                     v_cache=vd, v_view=view, v_scale=FP8_SCALE)
+        else:
+            pa.pa_reshape_and_cache(case.new_k, slots, kd, view, 0, case.block_size, case.num_blocks, v=case.new_v,
+                                    v_cache=vd, v_view=view)
         if ev is not None:
             ev[0].record(stream)
         pa.pa_decode(out, case.q, kd, vd, tables, lens, max_ctx, case.scale, desc, ws)
@@ -152,7 +197,7 @@ def run_dense(name, steps, warmup, partition):
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
     dec = tm.ms()
     dec_mean = float(np.mean(dec))
-    logical, unique, write = dense_bytes(case)
+    logical, unique, write = dense_bytes(case, row8)
     achieved = unique / (dec_mean / 1e3) / 1e9
     cow = {}
     if name == "gqa_prefix_copied":
@@ -175,6 +220,8 @@ def run_dense(name, steps, warmup, partition):
         cow = {"copy_on_write_pairs": len(pairs), "copy_on_write_ms": float(np.mean(ms)),
                "copy_on_write_gbs": cbytes / (np.mean(ms) / 1e3) / 1e9}
     kernel = "decode_mfma_kernel" if (D == 128 and Hq // case.num_kv_heads >= 2) else "decode_dense_kernel"
+    if fp8:
+        kernel = "decode_fp8_kernel"
     return case, {
         "workload": wdesc,
         "ms_per_step": ms_step,
@@ -186,8 +233,9 @@ def run_dense(name, steps, warmup, partition):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(name),
                      "kernel": f"pa_decode ({kernel} + decode_reduce_kernel)", "algorithmic_bytes_per_call": unique},
-        "dtype": case.dtype,
+        "dtype": "fp8-e4m3 K/V, bf16 q" if fp8 else case.dtype,
         **cow,
+        **quant,
         "config": {"num_seqs": B, "num_q_heads": Hq, "num_kv_heads": case.num_kv_heads, "head_dim": D,
                    "block_size": case.block_size, "num_blocks": case.num_blocks,
                    "sum_context_tokens": int(case.context_lens.sum()), "partition_size": part or "auto"},
@@ -435,15 +483,17 @@ def main():
     metric = "paged decode effective KV GB/s (% of HBM peak) and decode tokens/s at 1 GPU"
     res = {"metric": metric, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "data": "synthetic (seeded N(0,1) K/V/Q, seeded block tables)"}
-    if args.workload in ("mha13b", "gqa_prefix", "gqa_prefix_copied", "long_decode"):
+    if args.workload in ("mha13b", "gqa_prefix", "gqa_prefix_copied", "long_decode", "mha13b_fp8",
+                         "gqa_prefix_copied_fp8"):
         case, r = run_dense(args.workload, args.steps, args.warmup, args.partition)
         res.update({"value": r["value"], "unit": "GB/s", "ms_per_step": r["ms_per_step"], "dtype": r["dtype"],
                     "config": dict(workload=r["workload"], **r["config"]),
                     "decode_tokens_per_s": r["decode_tokens_per_s"], "decode_call_ms": r["decode_call_ms"],
                     "decode_call_ms_p10_p90": r["decode_call_ms_p10_p90"],
                     "decode_kv_gbs_logical": r["decode_kv_gbs_logical"], "roofline": r["roofline"]})
-        res.update({k: r[k] for k in ("copy_on_write_pairs", "copy_on_write_ms", "copy_on_write_gbs") if k in r})
-        if not args.no_cpu_baseline:
+        res.update({k: r[k] for k in ("copy_on_write_pairs", "copy_on_write_ms", "copy_on_write_gbs", "quantize_pool_ms",
+                                      "quantize_pool_gbs") if k in r})
+        if not args.no_cpu_baseline and case.k_pool is not None:
             res["cpu_baseline"] = cpu_baseline(case)
         del case
         torch.cuda.empty_cache()
@@ -458,12 +508,13 @@ def main():
 
     if args.workload == "mha13b" and not args.no_extra:
         extra = {}
-        for name in ("gqa_prefix_copied", "gqa_prefix", "long_decode"):
+        for name in ("gqa_prefix_copied", "gqa_prefix", "long_decode", "mha13b_fp8", "gqa_prefix_copied_fp8"):
             case, r = run_dense(name, 10, 3, 0)
             extra[name] = {"workload": r["workload"], "decode_call_ms": r["decode_call_ms"],
                            "kv_gbs": r["roofline"]["achieved"], "frac_of_hbm_peak": r["roofline"]["frac"],
                            "kv_gbs_logical": r["decode_kv_gbs_logical"], "decode_tokens_per_s": r["decode_tokens_per_s"]}
-            for k in ("copy_on_write_pairs", "copy_on_write_ms", "copy_on_write_gbs"):
+            for k in ("copy_on_write_pairs", "copy_on_write_ms", "copy_on_write_gbs", "quantize_pool_ms",
+                      "quantize_pool_gbs"):
                 if k in r:
                     extra[name][k] = r[k]
             del case

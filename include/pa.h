@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum pa_status {
     PA_OK = 0,
@@ -71,11 +71,17 @@ typedef enum pa_status {
  *     bf16 [.., num_q_heads, 576] (512 latent dims, then 64 RoPE dims).
  *     Outputs are bf16 [.., num_q_heads, 512]: the softmax-weighted
  *     dequantized latent ([MEM] §3.3: attention stays in latent space).
+ *   PA_KV_FP8_E4M3: dense rows as for PA_KV_BF16, one OCP e4m3 byte per value
+ *     ([MEM] §3.4: quantize on write, dequantize on read, FP8 the safest
+ *     format). Every K value is its code times pa_attn_desc.k_scale and every V
+ *     value its code times v_scale (one float32 scale per cache). Queries and
+ *     outputs are bf16. Written by pa_quantize_and_cache.
  */
 typedef enum pa_kv_format {
     PA_KV_F16 = 0,
     PA_KV_BF16 = 1,
-    PA_KV_MLA656_E4M3 = 2
+    PA_KV_MLA656_E4M3 = 2,
+    PA_KV_FP8_E4M3 = 3
 } pa_kv_format;
 
 /* One view over a flat cache allocation: the KVCacheTensor parameters of
@@ -112,6 +118,8 @@ typedef struct pa_attn_desc {
     pa_cache_view v_view;         /* V rows (dense only; ignored for MLA) */
     int64_t k_cache_bytes;        /* size of the allocation at k_cache, for the extent check */
     int64_t v_cache_bytes;        /* size of the allocation at v_cache (dense only) */
+    float k_scale;                /* PA_KV_FP8_E4M3 only: K value = code * k_scale (finite, > 0) */
+    float v_scale;                /* PA_KV_FP8_E4M3 only: V value = code * v_scale (finite, > 0) */
 } pa_attn_desc;
 
 /* ABI version of the loaded library (PA_ABI_VERSION). */
@@ -180,6 +188,24 @@ int32_t pa_quantize_and_cache_mla(const void* latent, int64_t latent_pitch, cons
                                   pa_cache_view mla_view, void* index_cache, int64_t index_cache_bytes,
                                   pa_cache_view index_view, int32_t layer, int32_t block_size,
                                   int64_t num_blocks, void* stream);
+
+/* pa_quantize_and_cache: quantize-on-write of dense K/V rows into a PA_KV_FP8_E4M3 cache.
+ *
+ * [MEM] §3.4: the cache may be stored at low precision by quantizing as it is written. Every value
+ * x of a source row (num_kv_heads * head_dim values of src_format, PA_KV_F16 or PA_KV_BF16) is
+ * stored as the OCP e4m3 code nearest to x / k_scale (x / v_scale for V), the quotient taken in
+ * float32, ties to the even mantissa, saturating at 448. The rows then land exactly where
+ * pa_reshape_and_cache puts them (view row_bytes = num_kv_heads * head_dim, one byte per value).
+ *   k, v           device rows; row t at k + t*k_pitch (bytes), 2*row_bytes bytes each. v may be NULL.
+ *   k_scale, v_scale  finite, > 0; the same values go into the pa_attn_desc of the decode.
+ *   Other arguments as for pa_reshape_and_cache.
+ * Inputs must be finite (otherwise the codes are unspecified). Alignment: sources and pitches 16
+ * bytes; cache bases, view offsets, strides and row_bytes 8 bytes. num_tokens == 0 is a no-op. */
+int32_t pa_quantize_and_cache(const void* k, int64_t k_pitch, const void* v, int64_t v_pitch, int32_t src_format,
+                              float k_scale, float v_scale, const int64_t* slot_mapping, int32_t num_tokens,
+                              void* k_cache, int64_t k_cache_bytes, pa_cache_view k_view, void* v_cache,
+                              int64_t v_cache_bytes, pa_cache_view v_view, int32_t layer, int32_t block_size,
+                              int64_t num_blocks, void* stream);
 
 /* pa_copy_blocks: the data movement of copy-on-write (and of any block move inside a pool).
  *

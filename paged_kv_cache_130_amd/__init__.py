@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     PagedAttentionError,
     PA_KV_BF16,
     PA_KV_F16,
+    PA_KV_FP8_E4M3,
     PA_KV_MLA656_E4M3,
     abi_version,
     dense_desc,
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     pa_decode_workspace_bytes,
     pa_prefill_chunk,
     pa_prefill_workspace_bytes,
+    pa_quantize_and_cache,
     pa_quantize_and_cache_mla,
     pa_reshape_and_cache,
     status_string,

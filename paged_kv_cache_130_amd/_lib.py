@@ -27,9 +27,10 @@ PA_ERR_HIP = 7
 PA_KV_F16 = 0
 PA_KV_BF16 = 1
 PA_KV_MLA656_E4M3 = 2
+PA_KV_FP8_E4M3 = 3
 
 EXPORTS = ("pa_abi_version", "pa_status_string", "pa_last_hip_error", "pa_reshape_and_cache", "pa_quantize_and_cache_mla",
-           "pa_copy_blocks",
+           "pa_copy_blocks", "pa_quantize_and_cache",
            "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_workspace_bytes", "pa_prefill_chunk")
 
 
@@ -43,7 +44,7 @@ class pa_attn_desc(ctypes.Structure):
                 ("qk_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("layer", ctypes.c_int32), ("partition_size", ctypes.c_int32), ("num_blocks", ctypes.c_int64),
                 ("k_view", pa_cache_view), ("v_view", pa_cache_view), ("k_cache_bytes", ctypes.c_int64),
-                ("v_cache_bytes", ctypes.c_int64)]
+                ("v_cache_bytes", ctypes.c_int64), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class PagedAttentionError(RuntimeError):
@@ -74,6 +75,8 @@ def _load():
         "pa_quantize_and_cache_mla": (I32, [P, I64, P, I64, P, I64, P, I32, P, I64, V, P, I64, V, I32, I32, I64,
                                             P]),
         "pa_copy_blocks": (I32, [P, I64, V, P, I64, V, P, I32, I32, I32, I64, P]),
+        "pa_quantize_and_cache": (I32, [P, I64, P, I64, I32, ctypes.c_float, ctypes.c_float, P, I32, P, I64, V, P, I64,
+                                        V, I32, I32, I64, P]),
         "pa_decode_workspace_bytes": (SZ, [ctypes.POINTER(pa_attn_desc), I32, I32]),
         "pa_decode": (I32, [P, P, P, P, P, I32, P, I32, I32, ctypes.c_float, ctypes.POINTER(pa_attn_desc), P, SZ,
                             P]),
@@ -133,12 +136,14 @@ class AttnDesc:
     v_cache_bytes: int = 0
     layer: int = 0
     partition_size: int = 0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     def c(self) -> pa_attn_desc:
         vv = self.v_view.c() if self.v_view is not None else pa_cache_view(0, 0, 0, 0, 0)
         return pa_attn_desc(self.kv_format, self.num_q_heads, self.num_kv_heads, self.qk_dim, self.v_dim,
                             self.block_size, self.layer, self.partition_size, self.num_blocks, self.k_view.c(), vv,
-                            self.k_cache_bytes, self.v_cache_bytes)
+                            self.k_cache_bytes, self.v_cache_bytes, self.k_scale, self.v_scale)
 
 
 def dense_view(block_size: int, num_kv_heads: int, head_dim: int, elem_bytes: int = 2) -> CacheView:
@@ -148,12 +153,15 @@ def dense_view(block_size: int, num_kv_heads: int, head_dim: int, elem_bytes: in
 
 
 def dense_desc(dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int, num_blocks: int,
-               k_cache_bytes: int, v_cache_bytes: int, partition_size: int = 0) -> AttnDesc:
-    v = dense_view(block_size, num_kv_heads, head_dim)
-    return AttnDesc(kv_format=PA_KV_F16 if dtype == "f16" else PA_KV_BF16, num_q_heads=num_q_heads,
+               k_cache_bytes: int, v_cache_bytes: int, partition_size: int = 0, k_scale: float = 1.0,
+               v_scale: float = 1.0) -> AttnDesc:
+    """dtype "f16" / "bf16" (16-bit caches) or "fp8" (E4M3 caches with k_scale / v_scale, bf16 queries)."""
+    fmt = {"f16": PA_KV_F16, "bf16": PA_KV_BF16, "fp8": PA_KV_FP8_E4M3}[dtype]
+    v = dense_view(block_size, num_kv_heads, head_dim, 1 if dtype == "fp8" else 2)
+    return AttnDesc(kv_format=fmt, num_q_heads=num_q_heads,
                     num_kv_heads=num_kv_heads, qk_dim=head_dim, v_dim=head_dim, block_size=block_size,
                     num_blocks=num_blocks, k_view=v, v_view=v, k_cache_bytes=k_cache_bytes,
-                    v_cache_bytes=v_cache_bytes, partition_size=partition_size)
+                    v_cache_bytes=v_cache_bytes, partition_size=partition_size, k_scale=k_scale, v_scale=v_scale)
 
 
 # --------------------------------------------------------------------------
@@ -228,6 +236,30 @@ def pa_quantize_and_cache_mla(latent, rope, slot_mapping, mla_cache, mla_view: C
                                         _nbytes(index_cache) if index_cache is not None else 0, iv, layer,
                                         block_size, num_blocks, _stream(stream))
     _check("pa_quantize_and_cache_mla", st)
+
+
+def pa_quantize_and_cache(k, slot_mapping, k_cache, k_view: CacheView, layer: int, block_size: int, num_blocks: int,
+                          k_scale: float, src_dtype: str = "bf16", v=None, v_cache=None, v_view: CacheView | None = None,
+                          v_scale: float = 1.0, stream=None):
+    """Quantize 16-bit K (and V) rows [T, Hkv*D] into FP8 E4M3 cache views (value = code * scale)."""
+    _require_device(k, slot_mapping, k_cache, v, v_cache)
+    if slot_mapping.dtype.itemsize != 8 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 tensor")
+    T = slot_mapping.numel()
+
+    def pitch(x, view):
+        if x.dim() != 2 or x.element_size() != 2 or x.stride(1) != 1 or x.shape[0] < T or x.shape[1] != view.row_bytes:
+            raise ValueError(f"expected a [>= {T}, {view.row_bytes}] 16-bit tensor with unit column stride")
+        return x.stride(0) * 2
+    kp = pitch(k, k_view)
+    vp = pitch(v, v_view) if v is not None else 0
+    vv = v_view.c() if v_view is not None else pa_cache_view(0, 0, 0, 0, 0)
+    fmt = PA_KV_F16 if src_dtype == "f16" else PA_KV_BF16
+    st = _lib.pa_quantize_and_cache(_ptr(k), kp, _ptr(v), vp, fmt, float(k_scale), float(v_scale), _ptr(slot_mapping),
+                                    T, _ptr(k_cache), _nbytes(k_cache), k_view.c(), _ptr(v_cache),
+                                    _nbytes(v_cache) if v_cache is not None else 0, vv, layer, block_size, num_blocks,
+                                    _stream(stream))
+    _check("pa_quantize_and_cache", st)
 
 
 def pa_copy_blocks(block_pairs, k_cache, k_view: CacheView, num_layers: int, block_size: int, num_blocks: int,

@@ -66,19 +66,24 @@ int32_t effective_partition(const pa_attn_desc& d) {
 }
 
 int32_t check_dense_desc(const pa_attn_desc& d) {
-    if (d.kv_format != PA_KV_F16 && d.kv_format != PA_KV_BF16) return PA_ERR_UNSUPPORTED;
+    if (d.kv_format != PA_KV_F16 && d.kv_format != PA_KV_BF16 && d.kv_format != PA_KV_FP8_E4M3)
+        return PA_ERR_UNSUPPORTED;
+    const bool fp8 = d.kv_format == PA_KV_FP8_E4M3;
+    if (fp8 && !(std::isfinite(d.k_scale) && d.k_scale > 0.f && std::isfinite(d.v_scale) && d.v_scale > 0.f))
+        return PA_ERR_INVALID_ARGUMENT;
     if (d.num_q_heads <= 0 || d.num_kv_heads <= 0 || d.num_q_heads % d.num_kv_heads != 0)
         return PA_ERR_INVALID_ARGUMENT;
     if (d.qk_dim != d.v_dim) return PA_ERR_INVALID_ARGUMENT;
     if (d.qk_dim != 64 && d.qk_dim != 128 && d.qk_dim != 256) return PA_ERR_UNSUPPORTED;
-    // Group sizes: any of 1..16 at head_dim 128 (matrix-core kernel for 2..16); 1, 2, 4 or 8 otherwise.
+    // Group sizes: any of 1..16 at head_dim 128 (matrix-core kernel for 2..16); 1, 2, 4 or 8 otherwise and
+    // for FP8 rows.
     const int32_t g = d.num_q_heads / d.num_kv_heads;
-    const bool g_ok = d.qk_dim == 128 ? (g >= 1 && g <= 16) : (g == 1 || g == 2 || g == 4 || g == 8);
+    const bool g_ok = (d.qk_dim == 128 && !fp8) ? (g >= 1 && g <= 16) : (g == 1 || g == 2 || g == 4 || g == 8);
     if (!g_ok) return PA_ERR_UNSUPPORTED;
     if (!block_size_ok(d.block_size)) return PA_ERR_UNSUPPORTED;
     if (d.partition_size < 0 || (d.partition_size > 0 && d.partition_size % d.block_size != 0))
         return PA_ERR_INVALID_ARGUMENT;
-    const int64_t row = (int64_t)d.num_kv_heads * d.qk_dim * 2;
+    const int64_t row = (int64_t)d.num_kv_heads * d.qk_dim * (fp8 ? 1 : 2);
     if (d.k_view.row_bytes != row || d.v_view.row_bytes != row) return PA_ERR_INVALID_ARGUMENT;
     int32_t st = check_view(d.k_view, d.layer, d.num_blocks, d.block_size, d.k_cache_bytes);
     if (st != PA_OK) return st;
@@ -273,6 +278,51 @@ int32_t pa_quantize_and_cache_mla(const void* latent, int64_t latent_pitch, cons
     return hip_status(pa::launch_quant_cache_write(p, static_cast<hipStream_t>(stream)));
 }
 
+int32_t pa_quantize_and_cache(const void* k, int64_t k_pitch, const void* v, int64_t v_pitch, int32_t src_format,
+                              float k_scale, float v_scale, const int64_t* slot_mapping, int32_t num_tokens,
+                              void* k_cache, int64_t k_cache_bytes, pa_cache_view k_view, void* v_cache,
+                              int64_t v_cache_bytes, pa_cache_view v_view, int32_t layer, int32_t block_size,
+                              int64_t num_blocks, void* stream) {
+    if (num_tokens < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !slot_mapping || !k_cache) return PA_ERR_NULL_POINTER;
+    if (v && !v_cache) return PA_ERR_NULL_POINTER;
+    if (src_format != PA_KV_F16 && src_format != PA_KV_BF16) return PA_ERR_UNSUPPORTED;
+    if (block_size <= 0 || num_blocks <= 0 || num_blocks > INT64_MAX / block_size) return PA_ERR_INVALID_ARGUMENT;
+    const int nviews = v ? 2 : 1;
+    const void* src[2] = {k, v};
+    const int64_t pitch[2] = {k_pitch, v_pitch};
+    void* base[2] = {k_cache, v_cache};
+    const int64_t bytes[2] = {k_cache_bytes, v_cache_bytes};
+    const pa_cache_view* view[2] = {&k_view, &v_view};
+    const float scale[2] = {k_scale, v_scale};
+    pa::QuantDenseParams p;
+    std::memset(&p, 0, sizeof(p));
+    for (int i = 0; i < nviews; ++i) {
+        if (!std::isfinite(scale[i]) || !(scale[i] > 0.f)) return PA_ERR_INVALID_ARGUMENT;
+        int32_t st = check_view(*view[i], layer, num_blocks, block_size, bytes[i]);
+        if (st != PA_OK) return st;
+        if (view[i]->row_bytes != k_view.row_bytes || view[i]->row_bytes % 8 != 0) return PA_ERR_INVALID_ARGUMENT;
+        if (pitch[i] < 2 * (int64_t)view[i]->row_bytes) return PA_ERR_INVALID_ARGUMENT;
+        if (!aligned(src[i], 16) || !aligned(pitch[i], 16) || !aligned(base[i], 8) || !view_aligned(*view[i], layer, 8))
+            return PA_ERR_MISALIGNED;
+        p.src[i] = static_cast<const char*>(src[i]);
+        p.pitch[i] = pitch[i];
+        p.dst[i] = static_cast<char*>(base[i]) + view[i]->offset + (int64_t)layer * view[i]->layer_stride;
+        p.block_stride[i] = view[i]->block_stride;
+        p.scale[i] = scale[i];
+        p.inv_scale[i] = 1.0f / scale[i];  // IEEE float division on the host: correctly rounded
+    }
+    p.slots = slot_mapping;
+    p.num_slots = num_blocks * block_size;
+    p.row_values = k_view.row_bytes;
+    p.num_tokens = num_tokens;
+    p.num_views = nviews;
+    p.block_size = block_size;
+    p.src_f16 = src_format == PA_KV_F16;
+    return hip_status(pa::launch_quant_dense_write(p, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pa_copy_blocks(void* k_cache, int64_t k_cache_bytes, pa_cache_view k_view, void* v_cache,
                        int64_t v_cache_bytes, pa_cache_view v_view, const int64_t* block_pairs, int32_t num_pairs,
                        int32_t num_layers, int32_t block_size, int64_t num_blocks, void* stream) {
@@ -310,7 +360,7 @@ int32_t pa_copy_blocks(void* k_cache, int64_t k_cache_bytes, pa_cache_view k_vie
 
 size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t max_context_len) {
     if (!desc || num_seqs <= 0 || max_context_len <= 0) return 0;
-    if (desc->kv_format == PA_KV_F16 || desc->kv_format == PA_KV_BF16) {
+    if (desc->kv_format == PA_KV_F16 || desc->kv_format == PA_KV_BF16 || desc->kv_format == PA_KV_FP8_E4M3) {
         if (!block_size_ok(desc->block_size)) return 0;
         return dense_decode_ws(*desc, num_seqs, max_context_len);
     }
@@ -404,9 +454,12 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
     p.max_parts = max_parts;
     p.max_context_len = max_context_len;
     p.scale_log2 = scale * 1.4426950408889634f;
-    p.is_bf16 = d.kv_format != PA_KV_F16;
+    p.is_bf16 = d.kv_format != PA_KV_F16;  // FP8 rows take bf16 queries and outputs
     p.head_dim = d.v_dim;
     p.group = d.num_q_heads / d.num_kv_heads;
+    p.kv_fp8 = d.kv_format == PA_KV_FP8_E4M3;
+    p.v_scale = p.kv_fp8 ? d.v_scale : 1.f;
+    if (p.kv_fp8) p.scale_log2 = scale * d.k_scale * 1.4426950408889634f;
     return hip_status(pa::launch_decode_dense(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -433,7 +486,7 @@ int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const vo
         return PA_ERR_NULL_POINTER;
     if (bt_stride <= 0 || !std::isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARGUMENT;
     const pa_attn_desc& d = *desc;
-    if (d.kv_format == PA_KV_MLA656_E4M3) return PA_ERR_UNSUPPORTED;
+    if (d.kv_format == PA_KV_MLA656_E4M3 || d.kv_format == PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
     int32_t st = check_dense_desc(d);
     if (st != PA_OK) return st;
     if (d.qk_dim != 128) return PA_ERR_UNSUPPORTED;  // causal chunks are implemented for head_dim 128

@@ -307,4 +307,129 @@ hipError_t launch_block_copy(const BlockCopyParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Quantize-on-write of dense rows into an FP8 cache.
+//
+// "deep dive into vLLM 05" §3.4: quantize on write, FP8. Every 16-bit value x of a row is stored as
+// the E4M3 code nearest to the float32 quotient x / scale (one scale per cache), ties to even,
+// saturating at 448. A wave takes the rows of 4 tokens as one run of 8-value units (16 bytes in,
+// 8 bytes out), loading a batch of units per lane before storing any; the quotients use the same
+// one-division-per-scale method as the DSA rows.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// 8 16-bit values -> 8 fp32 values (exact).
+template <bool F16>
+__device__ __forceinline__ void x16x8_to_f32(const uint4& v, float (&x)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (F16) {
+            x[2 * i] = (float)__builtin_bit_cast(f16x2, w[i]).x;
+            x[2 * i + 1] = (float)__builtin_bit_cast(f16x2, w[i]).y;
+        } else {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+}
+
+// Codes of 8 values for a fixed scale with its correctly rounded reciprocal (see quantize8).
+__device__ __forceinline__ uint2 quantize8_fixed(const float (&x)[8], float scale, float y) {
+    const bool normal = scale >= 1.17549435e-38f;
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float qq;
+            if (normal) {
+                const float q0 = x[4 * h + i] * y;
+                qq = __builtin_fmaf(__builtin_fmaf(-q0, scale, x[4 * h + i]), y, q0);
+            } else {
+                qq = __fdiv_rn(x[4 * h + i], scale);
+            }
+            q[i] = fminf(fmaxf(qq, -448.f), 448.f);
+        }
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], v, true);
+        w[h] = (uint32_t)v;
+    }
+    return make_uint2(w[0], w[1]);
+}
+
+template <bool F16>
+__device__ __forceinline__ void quant_rows(const QuantDenseParams& p, int view, int t0, int lane) {
+    constexpr int TPW = kCopyTokensPerWave;
+    const uint32_t n = (uint32_t)p.row_values / 8;  // 8-value units per row
+    const int ntok = min(TPW, p.num_tokens - t0);
+    const uint32_t total = (uint32_t)ntok * n;
+    const char* src = p.src[view] + (int64_t)t0 * p.pitch[view];
+    const int64_t my_slot = lane < ntok ? p.slots[t0 + lane] : -1;
+    const float scale = p.scale[view], y = p.inv_scale[view];
+
+    uint4 v[kCopyBatch];
+    uint32_t tok[kCopyBatch], c[kCopyBatch];
+    auto load_batch = [&](uint32_t base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u) {
+            const uint32_t j = min(base + 64 * u + lane, total - 1);  // past the end: a valid duplicate
+            tok[u] = j / n;
+            c[u] = j - tok[u] * n;
+            v[u] = reinterpret_cast<const uint4*>(src + (int64_t)tok[u] * p.pitch[view])[c[u]];
+        }
+    };
+    load_batch(0);
+    char* dst[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int64_t slot = (int64_t)((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)my_slot, i) |
+                                       ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_slot >> 32), i) << 32));
+        char* d = nullptr;
+        if (i < ntok && slot >= 0 && slot < p.num_slots) {
+            const int64_t block = slot / p.block_size;
+            d = p.dst[view] + block * p.block_stride[view] + (slot - block * p.block_size) * (int64_t)p.row_values;
+        }
+        dst[i] = d;
+    }
+    for (uint32_t base = 0;;) {
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u) {
+            if (base + 64 * u + lane >= total) continue;
+            float x[8];
+            x16x8_to_f32<F16>(v[u], x);
+            const uint2 codes = quantize8_fixed(x, scale, y);
+            char* d = dst[0];
+#pragma unroll
+            for (int i = 1; i < TPW; ++i) d = tok[u] == (uint32_t)i ? dst[i] : d;
+            if (d != nullptr) reinterpret_cast<uint2*>(d)[c[u]] = codes;
+        }
+        base += 64 * kCopyBatch;
+        if (base >= total) break;
+        load_batch(base);
+    }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void quant_dense_write_kernel(QuantDenseParams p) {
+    const int view = blockIdx.y;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int t0 = (blockIdx.x * 4 + wave) * kCopyTokensPerWave;
+    if (t0 >= p.num_tokens) return;
+    if (p.src_f16) quant_rows<true>(p, view, t0, lane);
+    else quant_rows<false>(p, view, t0, lane);
+}
+
+hipError_t launch_quant_dense_write(const QuantDenseParams& p, hipStream_t stream) {
+    if (p.num_tokens <= 0) return hipSuccess;
+    const int per_wg = 4 * kCopyTokensPerWave;
+    dim3 grid((p.num_tokens + per_wg - 1) / per_wg, p.num_views);
+    hipLaunchKernelGGL(quant_dense_write_kernel, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace pa

@@ -375,6 +375,7 @@ hipError_t launch_decode_reduce(const DenseDecodeParams& p, hipStream_t stream) 
 // head sizes run on the VALU kernel above.
 hipError_t launch_decode_dense(const DenseDecodeParams& p, hipStream_t stream) {
     if (p.num_seqs <= 0) return hipSuccess;
+    if (p.kv_fp8) return launch_decode_fp8(p, stream);
     if (p.head_dim == 128 && p.group >= 2) return launch_decode_mfma(p, stream);
     return p.is_bf16 ? launch_dim<true>(p, stream) : launch_dim<false>(p, stream);
 }

@@ -21,15 +21,15 @@ __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over aligned groups of N lanes (N = 8, 16, 32, 64); every lane of a group gets the group sum.
-// Within a 16-lane DPP row a butterfly of quad permutes and mirrors covers all lanes; wider
+// Sum over aligned groups of N lanes (N = 4, 8, 16, 32, 64); every lane of a group gets the group
+// sum. Within a 16-lane DPP row a butterfly of quad permutes and mirrors covers all lanes; wider
 // groups add cross-row shuffles.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-    static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group width");
+    static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group width");
     x += dpp_mov<kDppQuadXor1>(x);
     x += dpp_mov<kDppQuadXor2>(x);
-    x += dpp_mov<kDppRowHalfMirror>(x);
+    if constexpr (N >= 8) x += dpp_mov<kDppRowHalfMirror>(x);
     if constexpr (N >= 16) x += dpp_mov<kDppRowMirror>(x);
     if constexpr (N >= 32) x += __shfl_xor(x, 16);
     if constexpr (N >= 64) x += __shfl_xor(x, 32);

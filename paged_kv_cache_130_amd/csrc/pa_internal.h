@@ -43,6 +43,22 @@ struct QuantWriteParams {
 };
 hipError_t launch_quant_cache_write(const QuantWriteParams& p, hipStream_t stream);
 
+// Quantize-on-write of dense 16-bit K/V rows into E4M3 rows with one float32 scale per cache.
+struct QuantDenseParams {
+    const char* src[2];        // row t at src + t * pitch
+    int64_t pitch[2];
+    char* dst[2];              // cache base + view offset + layer * layer_stride
+    int64_t block_stride[2];
+    float scale[2];            // value = code * scale
+    float inv_scale[2];        // 1 / scale, correctly rounded
+    const int64_t* slots;
+    int64_t num_slots;
+    int32_t row_values;        // values per row (= bytes per cache row)
+    int32_t num_tokens, num_views, block_size;
+    int32_t src_f16;           // 1: fp16 sources, 0: bf16
+};
+hipError_t launch_quant_dense_write(const QuantDenseParams& p, hipStream_t stream);
+
 // Copy-on-write's data movement: for each (src, dst) block pair and each layer, copy the page
 // (block_size contiguous rows) of every view.
 struct BlockCopyParams {
@@ -86,8 +102,11 @@ struct DenseDecodeParams {
     int32_t is_bf16;
     int32_t head_dim;
     int32_t group;             // Hq / Hkv
+    int32_t kv_fp8;            // 1: E4M3 rows (one byte per value), bf16 queries and outputs
+    float v_scale;             // FP8 rows: V value = code * v_scale (K's scale is folded into scale_log2)
 };
 hipError_t launch_decode_dense(const DenseDecodeParams& p, hipStream_t stream);   // picks the kernel below
+hipError_t launch_decode_fp8(const DenseDecodeParams& p, hipStream_t stream);     // FP8 rows (decode_fp8.hip)
 hipError_t launch_decode_mfma(const DenseDecodeParams& p, hipStream_t stream);    // head_dim 128, group 2..16
 hipError_t launch_decode_reduce(const DenseDecodeParams& p, hipStream_t stream);  // partition merge
 

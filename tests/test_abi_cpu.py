@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
-    assert pa.abi_version() == 1
+    assert pa.abi_version() == 2
 
 
 def test_status_strings():
@@ -182,3 +182,33 @@ def test_copy_blocks_status_codes():
     assert copyb(pairs=FAKE + 4) == E.PA_ERR_MISALIGNED
     assert copyb(kview=pa.CacheView(2, 64 * 16 * 2048, 16 * 2048, 2048).c(), kb=3 * 64 * 16 * 2048 + 16) == \
         E.PA_ERR_MISALIGNED
+
+
+def qdense(k=FAKE, kp=4096, v=FAKE, vp=4096, fmt=None, ks=0.5, vs=0.5, slots=FAKE, T=4, kc=FAKE, kb=64 * 16 * 1024,
+           kview=None, vc=FAKE, vb=64 * 16 * 1024, vview=None, layer=0, bs=16, nb=64):
+    fmt = L.PA_KV_BF16 if fmt is None else fmt
+    kview = kview or pa.dense_view(16, 8, 128, 1).c()
+    vview = vview or pa.dense_view(16, 8, 128, 1).c()
+    return L._lib.pa_quantize_and_cache(k, kp, v, vp, fmt, ks, vs, slots, T, kc, kb, kview, vc, vb, vview, layer, bs,
+                                        nb, None)
+
+
+def test_fp8_status_codes():
+    E = L
+    assert qdense(T=0) == E.PA_OK
+    assert qdense(k=None) == E.PA_ERR_NULL_POINTER
+    assert qdense(vc=None) == E.PA_ERR_NULL_POINTER
+    assert qdense(fmt=L.PA_KV_FP8_E4M3) == E.PA_ERR_UNSUPPORTED          # sources are 16-bit
+    assert qdense(ks=0.0) == E.PA_ERR_INVALID_ARGUMENT
+    assert qdense(vs=float("inf")) == E.PA_ERR_INVALID_ARGUMENT
+    assert qdense(kp=1024) == E.PA_ERR_INVALID_ARGUMENT                  # pitch below one 16-bit row
+    assert qdense(kb=64 * 16 * 1024 - 1) == E.PA_ERR_VIEW_OUT_OF_RANGE
+    assert qdense(k=FAKE + 8) == E.PA_ERR_MISALIGNED
+    # decode descriptors of an FP8 cache
+    d = pa.dense_desc("fp8", 8, 8, 128, 16, 64, 64 * 16 * 1024, 64 * 16 * 1024, k_scale=0.5, v_scale=0.5)
+    assert decode(d) != E.PA_ERR_INVALID_ARGUMENT and decode(d) != E.PA_ERR_UNSUPPORTED
+    bad = pa.dense_desc("fp8", 8, 8, 128, 16, 64, 64 * 16 * 1024, 64 * 16 * 1024, k_scale=-1.0, v_scale=0.5)
+    assert decode(bad) == E.PA_ERR_INVALID_ARGUMENT
+    g16 = pa.dense_desc("fp8", 32, 2, 128, 16, 64, 64 * 16 * 256, 64 * 16 * 256, k_scale=0.5, v_scale=0.5)
+    assert decode(g16) == E.PA_ERR_UNSUPPORTED                           # group 16 is not an FP8 group size
+    assert pa.pa_decode_workspace_bytes(d, 4, 2048) > 0

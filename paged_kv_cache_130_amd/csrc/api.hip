@@ -75,10 +75,9 @@ int32_t check_dense_desc(const pa_attn_desc& d) {
         return PA_ERR_INVALID_ARGUMENT;
     if (d.qk_dim != d.v_dim) return PA_ERR_INVALID_ARGUMENT;
     if (d.qk_dim != 64 && d.qk_dim != 128 && d.qk_dim != 256) return PA_ERR_UNSUPPORTED;
-    // Group sizes: any of 1..16 at head_dim 128 (matrix-core kernel for 2..16); 1, 2, 4 or 8 otherwise and
-    // for FP8 rows.
+    // Group sizes: any of 1..16 at head_dim 128 (matrix-core kernel for 2..16); 1, 2, 4 or 8 otherwise.
     const int32_t g = d.num_q_heads / d.num_kv_heads;
-    const bool g_ok = (d.qk_dim == 128 && !fp8) ? (g >= 1 && g <= 16) : (g == 1 || g == 2 || g == 4 || g == 8);
+    const bool g_ok = d.qk_dim == 128 ? (g >= 1 && g <= 16) : (g == 1 || g == 2 || g == 4 || g == 8);
     if (!g_ok) return PA_ERR_UNSUPPORTED;
     if (!block_size_ok(d.block_size)) return PA_ERR_UNSUPPORTED;
     if (d.partition_size < 0 || (d.partition_size > 0 && d.partition_size % d.block_size != 0))

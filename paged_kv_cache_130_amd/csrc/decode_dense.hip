@@ -375,8 +375,10 @@ hipError_t launch_decode_reduce(const DenseDecodeParams& p, hipStream_t stream) 
 // head sizes run on the VALU kernel above.
 hipError_t launch_decode_dense(const DenseDecodeParams& p, hipStream_t stream) {
     if (p.num_seqs <= 0) return hipSuccess;
-    if (p.kv_fp8) return launch_decode_fp8(p, stream);
+    // Grouped heads at head_dim 128 (16-bit or FP8 rows) run on the matrix cores; the other FP8 shapes
+    // on the FP8 vector kernel.
     if (p.head_dim == 128 && p.group >= 2) return launch_decode_mfma(p, stream);
+    if (p.kv_fp8) return launch_decode_fp8(p, stream);
     return p.is_bf16 ? launch_dim<true>(p, stream) : launch_dim<false>(p, stream);
 }
 

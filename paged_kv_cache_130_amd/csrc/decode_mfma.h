@@ -31,6 +31,8 @@
 
 #pragma once
 
+#include <type_traits>
+
 #include "decode_common.h"
 #include "mfma_common.h"
 
@@ -89,11 +91,38 @@ __device__ __forceinline__ void mfma_tile_step(const uint4 (&kk)[4], uint4 (&vv)
     }
 }
 
+typedef float f32x2_dm_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2_dm_t __attribute__((ext_vector_type(2)));
+
+// 8 E4M3 codes -> 8 bf16 values (exact: an E4M3 value's fp32 form has its low 16 bits zero).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 w) {
+    const f32x2_dm_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false);
+    const f32x2_dm_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
+    const f32x2_dm_t c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false);
+    const f32x2_dm_t d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
+    auto hi2 = [](float x0, float x1) __attribute__((always_inline)) {
+        return __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), kSelHi);
+    };
+    return make_uint4(hi2(a.x, a.y), hi2(b.x, b.y), hi2(c.x, c.y), hi2(d.x, d.y));
+}
+
+__device__ __forceinline__ uint2 load_nt8(const char* ptr) {
+    const u32x2_dm_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_dm_t*>(ptr));
+    return make_uint2(a.x, a.y);
+}
+
 }  // namespace
 
 // One wave's work item of the grouped-query decode: item = (partition-major work index) * Hkv + K/V head.
-template <bool BF16>
+// FP8: E4M3 rows (one byte per value, bf16 queries and outputs). The same operand layouts are
+// loaded at half the width (8 bytes per lane instead of 16) and widened to bf16 when used, so the
+// products are those of the bf16 path on the exactly dequantized codes; K's scale is in
+// scale_log2 and V's multiplies the accumulators at the end.
+template <bool BF16, bool FP8 = false>
 __device__ __forceinline__ void decode_mfma_wave(const DenseDecodeParams& p, int item) {
+    static_assert(!FP8 || BF16, "FP8 rows take bf16 queries");
+    using Raw = std::conditional_t<FP8, uint2, uint4>;
+    constexpr int kEsz = FP8 ? 1 : 2;  // bytes per cached value
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4;
     const int c = lane & 15;
@@ -135,30 +164,36 @@ __device__ __forceinline__ void decode_mfma_wave(const DenseDecodeParams& p, int
     const int tbl = lane < nblk ? bt[lb0 + lane] : 0;
 
     const int64_t krow = p.k_row_bytes, vrow = p.v_row_bytes;
-    // K: token sigma(c), bytes 16*g4 (+64 per k-step); V: token g4 (+4 per load), bytes 16*c.
-    const uint32_t klane = (uint32_t)(kvh * (kD * 2) + 16 * g4) + (uint32_t)sigma(c) * (uint32_t)krow;
-    const uint32_t vlane = (uint32_t)(kvh * (kD * 2) + 16 * c) + (uint32_t)g4 * (uint32_t)vrow;
+    // K: token sigma(c), dims 8*g4 (+32 per k-step); V: token g4 (+4 per load), dims 8*c.
+    const uint32_t klane = (uint32_t)(kvh * (kD * kEsz) + 8 * kEsz * g4) + (uint32_t)sigma(c) * (uint32_t)krow;
+    const uint32_t vlane = (uint32_t)(kvh * (kD * kEsz) + 8 * kEsz * c) + (uint32_t)g4 * (uint32_t)vrow;
     const uint32_t nb = (uint32_t)p.num_blocks;
     const int ntiles = (te - tb + 15) >> 4;
     const int last = ntiles - 1;
     const char* dummy = reinterpret_cast<const char*>(qrow);
 
     auto block_of = [&](int j) { return __builtin_amdgcn_readlane(tbl, j >> tpb_log2); };
-    auto load = [&](uint4 (&kk)[4], uint4 (&vv)[4], int j) {
+    auto load = [&](Raw (&kk)[4], Raw (&vv)[4], int j) {
         const bool real = j <= last;
         int phys = block_of(real ? j : last);
         phys = ((uint32_t)phys < nb) ? phys : 0;
         const int64_t row0 = (int64_t)((j & tpb_mask) << 4);
         const char* kt = real ? p.k + (int64_t)phys * p.k_block_stride + row0 * krow : dummy;
         const char* vt = real ? p.v + (int64_t)phys * p.v_block_stride + row0 * vrow : dummy;
-        const int64_t kstep = real ? 64 : 0, vstep = real ? 4 * vrow : 0;
+        const int64_t kstep = real ? 32 * kEsz : 0, vstep = real ? 4 * vrow : 0;
         const uint32_t ko = real ? klane : 0u, vo = real ? vlane : 0u;
-        // K through the cache: an operand load covers 64 of a row's bytes, so each 128-byte line is
-        // shared by two consecutive loads. V (16 contiguous bytes per lane) streams nontemporally.
+        // K through the cache: an operand load covers a quarter or half of a head's row, so the row's
+        // lines are shared by consecutive loads. V (whole head rows per lane group) streams
+        // nontemporally.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            kk[i] = *reinterpret_cast<const uint4*>(kt + i * kstep + ko);
-            vv[i] = load_nt16(vt + i * vstep + vo);
+            if constexpr (FP8) {
+                kk[i] = *reinterpret_cast<const uint2*>(kt + i * kstep + ko);
+                vv[i] = load_nt8(vt + i * vstep + vo);
+            } else {
+                kk[i] = *reinterpret_cast<const uint4*>(kt + i * kstep + ko);
+                vv[i] = load_nt16(vt + i * vstep + vo);
+            }
         }
     };
 
@@ -166,13 +201,23 @@ __device__ __forceinline__ void decode_mfma_wave(const DenseDecodeParams& p, int
     f32x4_t O[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) O[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    auto step = [&](const uint4 (&kk)[4], uint4 (&vv)[4], int j) {
+    auto step = [&](const Raw (&kk)[4], Raw (&vv)[4], int j) {
         int nvalid = min(16, te - (tb + (j << 4)));
         if ((uint32_t)block_of(j) >= nb) nvalid = 0;
-        mfma_tile_step<BF16>(kk, vv, qb, m, l, O, g4, nvalid, p.scale_log2);
+        if constexpr (FP8) {
+            uint4 kw[4], vw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kw[i] = e4m3x8_to_bf16(kk[i]);
+                vw[i] = e4m3x8_to_bf16(vv[i]);
+            }
+            mfma_tile_step<true>(kw, vw, qb, m, l, O, g4, nvalid, p.scale_log2);
+        } else {
+            mfma_tile_step<BF16>(kk, vv, qb, m, l, O, g4, nvalid, p.scale_log2);
+        }
     };
 
-    uint4 k0[4], v0[4], k1[4], v1[4];
+    Raw k0[4], v0[4], k1[4], v1[4];
     load(k0, v0, 0);
     for (int j = 0; j < ntiles; j += 2) {
         load(k1, v1, j + 1);
@@ -190,6 +235,10 @@ __device__ __forceinline__ void decode_mfma_wave(const DenseDecodeParams& p, int
         const float L = __shfl(l, h);
         const float M = __shfl(m, h);
         if (h >= G) continue;
+        if constexpr (FP8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) O[e][j] *= p.v_scale;
+        }
         if (nparts == 1) {
             const float inv = 1.f / L;
             uint4 o;

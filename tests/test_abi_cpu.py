@@ -209,6 +209,6 @@ def test_fp8_status_codes():
     assert decode(d) != E.PA_ERR_INVALID_ARGUMENT and decode(d) != E.PA_ERR_UNSUPPORTED
     bad = pa.dense_desc("fp8", 8, 8, 128, 16, 64, 64 * 16 * 1024, 64 * 16 * 1024, k_scale=-1.0, v_scale=0.5)
     assert decode(bad) == E.PA_ERR_INVALID_ARGUMENT
-    g16 = pa.dense_desc("fp8", 32, 2, 128, 16, 64, 64 * 16 * 256, 64 * 16 * 256, k_scale=0.5, v_scale=0.5)
-    assert decode(g16) == E.PA_ERR_UNSUPPORTED                           # group 16 is not an FP8 group size
+    g16 = pa.dense_desc("fp8", 32, 2, 64, 16, 64, 64 * 16 * 128, 64 * 16 * 128, k_scale=0.5, v_scale=0.5)
+    assert decode(g16) == E.PA_ERR_UNSUPPORTED                           # group 16 needs head_dim 128
     assert pa.pa_decode_workspace_bytes(d, 4, 2048) > 0

@@ -4,7 +4,8 @@
 case quantizes a whole 16-bit pool through pa_quantize_and_cache (every slot in order), checks every
 byte against the oracle's quantization, NaN-poisons the rows past each context and the unused
 blocks (E4M3 code 0x7F), then decodes with bf16 queries and compares with the oracle's float64
-decode of the same bytes (codes times the cache scales) at the dense tolerance.
+decode of the same bytes (codes times the cache scales) at the dense tolerance. Groups of 2..16
+query heads at head_dim 128 run on the matrix cores, the other shapes on the FP8 vector kernel.
 """
 
 import numpy as np
@@ -87,6 +88,8 @@ SHAPES = [
     (8, 1, 128, 64, [63, 64, 65, 3000], 0),
     (4, 4, 128, 32, [0, 31, 33, 1000], 64),
     (8, 8, 64, 16, [2, 3, 5], 0),
+    (32, 2, 128, 16, [7, 300, 1100], 0),      # group 16, matrix cores
+    (24, 8, 128, 16, [2, 3, 4, 5, 33], 0),    # group 3, matrix cores, short rows
 ]
 
 

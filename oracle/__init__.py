@@ -19,6 +19,9 @@ kernel error. It computes:
 * ``attention``: paged decode (dense and grouped heads), causal chunks over
   paged context, MLA latent decode, and the log-sum-exp merge of
   split-context partials.
+* ``dsa``: the sparse path over the DSA dual cache: lightning-indexer scores
+  from the indexer rows, the top-k selection, and MLA decode over the
+  selected slots.
 
 Sources. These are the four pages on vLLM's KV cache, cited by title:
 
@@ -32,4 +35,4 @@ the pages' worked numbers, closed forms, torch library routines, or brute
 force. No function is parity-unpinned.
 """
 
-from . import numerics, paging, cache_write, attention, quant  # noqa: F401
+from . import numerics, paging, cache_write, attention, quant, dsa  # noqa: F401

@@ -130,3 +130,50 @@ def test_swapped_fp8_scales_are_caught(monkeypatch):
         return orig(*args, k_scale=v_scale, v_scale=k_scale, **kw)
     monkeypatch.setattr(A, "paged_decode", swapped)
     _fails(TA.test_fp8_cache_decode_equals_bf16_decode_of_the_dequantized_values)
+
+
+def test_dropped_indexer_relu_is_caught(monkeypatch):
+    from oracle import dsa as D
+    import test_oracle_dsa as TD
+
+    def no_relu(q_bits, weights, rows):
+        q = D.bf16_bits_to_f64(np.asarray(q_bits, dtype=np.uint16))
+        return (D.index_keys(rows) @ q.T) @ np.asarray(weights, dtype=np.float64)
+    monkeypatch.setattr(D, "index_scores_of_rows", no_relu)
+    _fails(TD.test_one_hot_keys_closed_form)
+
+
+def test_indexer_weights_on_the_wrong_heads_are_caught(monkeypatch):
+    from oracle import dsa as D
+    import test_oracle_dsa as TD
+    orig = D.index_scores_of_rows
+    monkeypatch.setattr(D, "index_scores_of_rows", lambda q, w, rows: orig(q, np.asarray(w)[::-1], rows))
+    _fails(TD.test_one_hot_keys_closed_form)
+
+
+def test_dropped_index_key_scale_is_caught(monkeypatch):
+    from oracle import dsa as D
+    import test_oracle_dsa as TD
+    monkeypatch.setattr(D, "index_keys", lambda rows: D.e4m3_bytes_to_f64(np.asarray(rows)[:, :128]))
+    _fails(TD.test_index_keys_match_torch_fp8_decoding)
+
+
+def test_later_position_winning_ties_is_caught(monkeypatch):
+    from oracle import dsa as D
+    import test_oracle_dsa as TD
+
+    def later_first(scores, top_k):
+        n = len(scores)
+        if top_k >= n:
+            return np.arange(n, dtype=np.int64)
+        ranked = sorted(range(n), key=lambda t: (-float(scores[t]), -t))
+        return np.sort(np.array(ranked[:top_k], dtype=np.int64))
+    monkeypatch.setattr(D, "topk_positions", later_first)
+    _fails(TD.test_topk_ties_prefer_earlier_positions)
+
+
+def test_neighbouring_row_in_sparse_decode_is_caught(monkeypatch):
+    from oracle import dsa as D
+    import test_oracle_dsa as TD
+    monkeypatch.setattr(D, "split_slot", lambda slot, bs: (int(slot) // int(bs), (int(slot) + 1) % int(bs)))
+    _fails(TD.test_sparse_decode_over_every_position_is_the_dense_decode)

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum pa_status {
     PA_OK = 0,
@@ -282,6 +282,66 @@ int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const vo
                          int32_t max_query_len, int32_t max_seq_len, float scale,
                          const pa_attn_desc* desc, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* pa_indexer_topk: lightning-indexer scores over the indexer view of the DSA dual cache, then each
+ * sequence's top-k token selection.
+ *
+ * [LAYOUT] (two caches sharing one block table): the lightning indexer stores per token a 132-byte
+ * row (128 OCP e4m3 key values, then one float32 scale) used to select a sparse top-k set of tokens;
+ * the indexer and MLA views share one block table. The pages give no scoring formula; this call
+ * computes the published lightning indexer's. For decode token b with index queries q[b, j]
+ * (j < num_index_heads, 128 bf16 values each) and head weights w[b, j] (float32), the score of
+ * context position t is
+ *     I[b, t] = sum_j w[b, j] * max(q[b, j] . k_t, 0),   k_t = codes_t * scale_t,
+ * read through the block table as pa_decode reads K. It is computed as
+ * scale_t * sum_j w[b, j] * max(q[b, j] . codes_t, 0) in float32 (equal for scale_t >= 0, which is
+ * what pa_quantize_and_cache_mla stores). The top_k positions of highest score are selected; equal
+ * scores are taken from the earliest position first, and when the context has at most top_k tokens
+ * every one is selected.
+ *
+ *   topk_positions device int32 [num_seqs, top_k]: the selected positions in ascending order; -1
+ *                  past topk_lens[b].
+ *   topk_slots     device int32 [num_seqs, top_k]: slot of each selected position
+ *                  (block_tables[b][t / block_size] * block_size + t % block_size), -1 past
+ *                  topk_lens[b] and for an invalid block id. These feed pa_mla_sparse_decode.
+ *   topk_lens      device int32 [num_seqs]: min(top_k, context length).
+ *   scores         device float32 [num_seqs, score_stride], score_stride >= max_context_len:
+ *                  written with I[b, t] for t < context length (-inf for positions in an invalid
+ *                  block); the other entries are untouched.
+ *   q_index        device bf16 [num_seqs, num_index_heads, 128]; head_weights device float32
+ *                  [num_seqs, num_index_heads]. num_index_heads: 16, 32, 48 or 64.
+ *   index_cache, index_cache_bytes, index_view, layer  the indexer view (row_bytes 132).
+ *   block_tables, bt_stride, context_lens, max_context_len, block_size, num_blocks  as for pa_decode.
+ * num_blocks * block_size must fit in int32. Scores are unspecified for non-finite inputs or a
+ * negative scale (memory-safe). Alignment: q_index 16 bytes; everything else 4 bytes.
+ * num_seqs == 0 is a no-op. */
+int32_t pa_indexer_topk(int32_t* topk_positions, int32_t* topk_slots, int32_t* topk_lens, int32_t top_k,
+                        float* scores, int64_t score_stride, const void* q_index, const float* head_weights,
+                        int32_t num_index_heads, const void* index_cache, int64_t index_cache_bytes,
+                        pa_cache_view index_view, int32_t layer, const int32_t* block_tables, int32_t bt_stride,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                        int32_t block_size, int64_t num_blocks, void* stream);
+
+/* pa_mla_sparse_decode: MLA decode over a selected set of cache rows (DSA sparse attention).
+ *
+ * The MLA decode of pa_decode ([MEM] §3.3, row format PA_KV_MLA656_E4M3), except that sequence b
+ * attends only to the rows at slots[b * slot_stride + i], i < slot_counts[b] (one softmax over
+ * them), each at block = slot / block_size, position = slot % block_size of the desc's view
+ * ([LAYOUT], section "kernel 那一侧"). A slot outside [0, num_blocks * block_size) contributes no
+ * token; no valid slot gives an output of 0. [LAYOUT] (two caches sharing one block table) has the
+ * indexer pick these tokens: pa_indexer_topk writes slots and counts in this form.
+ *
+ *   out, q         as for an MLA pa_decode: bf16 [num_seqs, num_q_heads, 512] and [.., 576].
+ *   kv_cache       allocation base of desc->k_view (desc->kv_format must be PA_KV_MLA656_E4M3).
+ *   slots          device int32 [num_seqs, slot_stride]; slot_counts device int32 [num_seqs], each
+ *                  clamped to [0, min(max_count, slot_stride)].
+ *   workspace      at least pa_decode_workspace_bytes(desc, num_seqs, max_count) bytes.
+ * num_blocks * block_size must fit in int32. Alignment: out, q, kv_cache and the view 16 bytes;
+ * slots and slot_counts 4 bytes. num_seqs == 0 is a no-op. */
+int32_t pa_mla_sparse_decode(void* out, const void* q, const void* kv_cache, const int32_t* slots,
+                             int32_t slot_stride, const int32_t* slot_counts, int32_t num_seqs, int32_t max_count,
+                             float scale, const pa_attn_desc* desc, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 #ifdef __cplusplus
 }

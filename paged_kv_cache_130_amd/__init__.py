@@ -19,6 +19,8 @@ from ._lib import (  # noqa: F401
     pa_copy_blocks,
     pa_decode,
     pa_decode_workspace_bytes,
+    pa_indexer_topk,
+    pa_mla_sparse_decode,
     pa_prefill_chunk,
     pa_prefill_workspace_bytes,
     pa_quantize_and_cache,

@@ -31,7 +31,8 @@ PA_KV_FP8_E4M3 = 3
 
 EXPORTS = ("pa_abi_version", "pa_status_string", "pa_last_hip_error", "pa_reshape_and_cache", "pa_quantize_and_cache_mla",
            "pa_copy_blocks", "pa_quantize_and_cache",
-           "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_workspace_bytes", "pa_prefill_chunk")
+           "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_workspace_bytes", "pa_prefill_chunk",
+           "pa_indexer_topk", "pa_mla_sparse_decode")
 
 
 class pa_cache_view(ctypes.Structure):
@@ -83,6 +84,9 @@ def _load():
         "pa_prefill_workspace_bytes": (SZ, [ctypes.POINTER(pa_attn_desc), I32, I32, I32, I32]),
         "pa_prefill_chunk": (I32, [P, P, P, P, P, I32, P, P, I32, I32, I32, I32, ctypes.c_float,
                                    ctypes.POINTER(pa_attn_desc), P, SZ, P]),
+        "pa_indexer_topk": (I32, [P, P, P, I32, P, I64, P, P, I32, P, I64, V, I32, P, I32, P, I32, I32, I32, I64, P]),
+        "pa_mla_sparse_decode": (I32, [P, P, P, P, I32, P, I32, I32, ctypes.c_float, ctypes.POINTER(pa_attn_desc), P,
+                                       SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -313,3 +317,48 @@ def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, seq_lens, query_sta
                                int(max_query_len), int(max_seq_len), float(scale), ctypes.byref(d), _ptr(workspace),
                                ws_bytes, _stream(stream))
     _check("pa_prefill_chunk", st)
+
+
+def pa_indexer_topk(topk_positions, topk_slots, topk_lens, scores, q_index, head_weights, index_cache,
+                    index_view: CacheView, layer: int, block_tables, context_lens, max_context_len: int,
+                    block_size: int, num_blocks: int, stream=None):
+    """Indexer scores (written into scores [B, >= max_context_len] float32) and each sequence's top-k.
+
+    topk_positions / topk_slots: int32 [B, top_k]; topk_lens int32 [B]; q_index bf16 [B, H, 128];
+    head_weights float32 [B, H].
+    """
+    _require_device(topk_positions, topk_slots, topk_lens, scores, q_index, head_weights, index_cache, block_tables,
+                    context_lens)
+    for name, t in (("topk_positions", topk_positions), ("topk_slots", topk_slots), ("topk_lens", topk_lens),
+                    ("q_index", q_index), ("head_weights", head_weights), ("block_tables", block_tables),
+                    ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if scores.dim() != 2 or scores.stride(1) != 1 or scores.element_size() != 4:
+        raise ValueError("scores must be a float32 [B, n] tensor with unit column stride")
+    B = context_lens.numel()
+    top_k = topk_positions.shape[1]
+    if topk_slots.shape[1] != top_k or q_index.shape[0] < B or q_index.shape[-1] != 128:
+        raise ValueError("inconsistent shapes")
+    st = _lib.pa_indexer_topk(_ptr(topk_positions), _ptr(topk_slots), _ptr(topk_lens), top_k, _ptr(scores),
+                              scores.stride(0), _ptr(q_index), _ptr(head_weights), q_index.shape[1],
+                              _ptr(index_cache), _nbytes(index_cache), index_view.c(), layer, _ptr(block_tables),
+                              block_tables.shape[1], _ptr(context_lens), B, int(max_context_len), block_size,
+                              num_blocks, _stream(stream))
+    _check("pa_indexer_topk", st)
+
+
+def pa_mla_sparse_decode(out, q, kv_cache, slots, slot_counts, max_count: int, scale: float, desc: AttnDesc,
+                         workspace=None, stream=None):
+    """MLA decode of sequence b over the rows at slots[b, :slot_counts[b]] (int32 slots [B, n])."""
+    _require_device(out, q, kv_cache, slots, slot_counts, workspace)
+    for name, t in (("out", out), ("q", q), ("slots", slots), ("slot_counts", slot_counts)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    d = desc.c()
+    B = slot_counts.numel()
+    ws_bytes = _nbytes(workspace) if workspace is not None else 0
+    st = _lib.pa_mla_sparse_decode(_ptr(out), _ptr(q), _ptr(kv_cache), _ptr(slots), slots.shape[1],
+                                   _ptr(slot_counts), B, int(max_count), float(scale), ctypes.byref(d),
+                                   _ptr(workspace), ws_bytes, _stream(stream))
+    _check("pa_mla_sparse_decode", st)

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
 SOURCES = ["api.hip", "cache_write.hip", "decode_dense.hip", "decode_fp8.hip", "decode_mfma.hip", "prefill_mfma.hip",
-           "decode_mla.hip"]
+           "decode_mla.hip", "dsa_indexer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

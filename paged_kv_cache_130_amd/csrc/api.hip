@@ -159,6 +159,46 @@ size_t mla_decode_ws(const MlaLayout& L, int32_t num_q_heads, int32_t num_seqs) 
     return (size_t)L.slots * num_q_heads * (512 + 2) * sizeof(float) + (size_t)num_seqs * 2 * sizeof(int32_t);
 }
 
+// The MLA decode, dense (through block_tables) or sparse (through slots); the descriptor and the
+// common pointers are already checked.
+int32_t mla_decode_call(void* out, const void* q, const void* k_cache, const int32_t* block_tables,
+                        int32_t bt_stride, const int32_t* slots, int64_t slot_stride, const int32_t* lens,
+                        int32_t num_seqs, int32_t max_len, float scale, const pa_attn_desc& d, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    MlaLayout L;
+    if (!mla_layout(d, num_seqs, max_len, L)) return PA_ERR_UNSUPPORTED;
+    const size_t need = mla_decode_ws(L, d.num_q_heads, num_seqs);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PA_ERR_MISALIGNED;
+    pa::MlaDecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.out = out;
+    p.q = q;
+    p.kv = static_cast<const char*>(k_cache) + d.k_view.offset + (int64_t)d.layer * d.k_view.layer_stride;
+    p.block_tables = block_tables;
+    p.context_lens = lens;
+    float* ws = static_cast<float*>(workspace);
+    p.part_acc = ws;
+    p.part_ml = ws + L.slots * d.num_q_heads * 512;
+    p.seq_meta = reinterpret_cast<int32_t*>(p.part_ml + L.slots * d.num_q_heads * 2);
+    p.block_stride = d.k_view.block_stride;
+    p.num_blocks = d.num_blocks;
+    p.bt_stride = bt_stride;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = d.num_q_heads;
+    p.heads_per_wg = L.heads_per_wg;
+    p.block_size = d.block_size;
+    p.block_size_log2 = log2_int(d.block_size);
+    p.max_context_len = max_len;
+    p.num_wgs = L.num_wgs;
+    p.units_per_wg = L.units_per_wg;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.slots = slots;
+    p.slot_stride = slot_stride;
+    p.num_slots = d.num_blocks * d.block_size;
+    return hip_status(pa::launch_decode_mla(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t dense_decode_ws(const pa_attn_desc& d, int32_t num_seqs, int32_t max_context_len) {
     const int32_t P = effective_partition(d);
     const int64_t parts = ((int64_t)max_context_len + P - 1) / P;
@@ -388,37 +428,9 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || (!mla && !aligned(v_cache, 16)) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return PA_ERR_MISALIGNED;
-    if (mla) {
-        MlaLayout L;
-        if (!mla_layout(d, num_seqs, max_context_len, L)) return PA_ERR_UNSUPPORTED;
-        const size_t need = mla_decode_ws(L, d.num_q_heads, num_seqs);
-        if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-        if (!aligned(workspace, 16)) return PA_ERR_MISALIGNED;
-        pa::MlaDecodeParams p;
-        std::memset(&p, 0, sizeof(p));
-        p.out = out;
-        p.q = q;
-        p.kv = static_cast<const char*>(k_cache) + d.k_view.offset + (int64_t)d.layer * d.k_view.layer_stride;
-        p.block_tables = block_tables;
-        p.context_lens = context_lens;
-        float* ws = static_cast<float*>(workspace);
-        p.part_acc = ws;
-        p.part_ml = ws + L.slots * d.num_q_heads * 512;
-        p.seq_meta = reinterpret_cast<int32_t*>(p.part_ml + L.slots * d.num_q_heads * 2);
-        p.block_stride = d.k_view.block_stride;
-        p.num_blocks = d.num_blocks;
-        p.bt_stride = bt_stride;
-        p.num_seqs = num_seqs;
-        p.num_q_heads = d.num_q_heads;
-        p.heads_per_wg = L.heads_per_wg;
-        p.block_size = d.block_size;
-        p.block_size_log2 = log2_int(d.block_size);
-        p.max_context_len = max_context_len;
-        p.num_wgs = L.num_wgs;
-        p.units_per_wg = L.units_per_wg;
-        p.scale_log2 = scale * 1.4426950408889634f;
-        return hip_status(pa::launch_decode_mla(p, static_cast<hipStream_t>(stream)));
-    }
+    if (mla)
+        return mla_decode_call(out, q, k_cache, block_tables, bt_stride, nullptr, 0, context_lens, num_seqs,
+                               max_context_len, scale, d, workspace, workspace_bytes, stream);
     const int32_t P = effective_partition(d);
     const int64_t max_parts64 = ((int64_t)max_context_len + P - 1) / P;
     const int32_t max_parts = max_parts64 < 1 ? 1 : (int32_t)max_parts64;
@@ -570,6 +582,78 @@ int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const vo
     st = hip_status(pa::launch_decode_dense(dp, s));
     if (st != PA_OK || max_query_len < 2) return st;
     return hip_status(pa::launch_prefill_chunk(pp, s));
+}
+
+int32_t pa_mla_sparse_decode(void* out, const void* q, const void* kv_cache, const int32_t* slots, int32_t slot_stride,
+                             const int32_t* slot_counts, int32_t num_seqs, int32_t max_count, float scale,
+                             const pa_attn_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!desc) return PA_ERR_NULL_POINTER;
+    if (num_seqs < 0 || max_count < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !q || !kv_cache || !slots || !slot_counts) return PA_ERR_NULL_POINTER;
+    if (slot_stride <= 0 || !std::isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARGUMENT;
+    const pa_attn_desc& d = *desc;
+    if (d.kv_format != PA_KV_MLA656_E4M3) return PA_ERR_UNSUPPORTED;
+    const int32_t st = check_mla_desc(d);
+    if (st != PA_OK) return st;
+    if (d.num_blocks * d.block_size > 0x7FFFFFFFLL) return PA_ERR_UNSUPPORTED;  // slots are int32
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(slots, 4) ||
+        !aligned(slot_counts, 4))
+        return PA_ERR_MISALIGNED;
+    return mla_decode_call(out, q, kv_cache, nullptr, 0, slots, slot_stride, slot_counts, num_seqs,
+                           std::min(max_count, slot_stride), scale, d, workspace, workspace_bytes, stream);
+}
+
+int32_t pa_indexer_topk(int32_t* topk_positions, int32_t* topk_slots, int32_t* topk_lens, int32_t top_k, float* scores,
+                        int64_t score_stride, const void* q_index, const float* head_weights, int32_t num_index_heads,
+                        const void* index_cache, int64_t index_cache_bytes, pa_cache_view index_view, int32_t layer,
+                        const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t max_context_len, int32_t block_size, int64_t num_blocks,
+                        void* stream) {
+    if (num_seqs < 0 || max_context_len < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_seqs == 0) return PA_OK;
+    if (!topk_positions || !topk_slots || !topk_lens || !scores || !q_index || !head_weights || !index_cache ||
+        !block_tables || !context_lens)
+        return PA_ERR_NULL_POINTER;
+    if (top_k <= 0 || bt_stride <= 0 || score_stride < std::max(1, max_context_len)) return PA_ERR_INVALID_ARGUMENT;
+    if (num_index_heads != 16 && num_index_heads != 32 && num_index_heads != 48 && num_index_heads != 64)
+        return PA_ERR_UNSUPPORTED;
+    if (!block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+    if (index_view.row_bytes != kIndexRowBytes) return PA_ERR_INVALID_ARGUMENT;
+    const int32_t st = check_view(index_view, layer, num_blocks, block_size, index_cache_bytes);
+    if (st != PA_OK) return st;
+    if (num_blocks * block_size > 0x7FFFFFFFLL) return PA_ERR_UNSUPPORTED;  // slots are int32
+    if ((int64_t)num_seqs * top_k > 0x7FFFFFFFLL || (int64_t)num_seqs > 0x7FFFFFFFLL / 64) return PA_ERR_UNSUPPORTED;
+    if (!aligned(q_index, 16) || !aligned(index_cache, 4) || !view_aligned(index_view, layer, 4) ||
+        !aligned(head_weights, 4) || !aligned(scores, 4) || !aligned(topk_positions, 4) ||
+        !aligned(topk_slots, 4) || !aligned(topk_lens, 4) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return PA_ERR_MISALIGNED;
+    pa::IndexerParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.idx = static_cast<const char*>(index_cache) + index_view.offset + (int64_t)layer * index_view.layer_stride;
+    p.q = static_cast<const uint16_t*>(q_index);
+    p.w = head_weights;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.scores = scores;
+    p.topk_pos = topk_positions;
+    p.topk_slots = topk_slots;
+    p.topk_lens = topk_lens;
+    p.score_stride = score_stride;
+    p.block_stride = index_view.block_stride;
+    p.num_blocks = num_blocks;
+    p.bt_stride = bt_stride;
+    p.num_seqs = num_seqs;
+    p.num_heads = num_index_heads;
+    p.block_size = block_size;
+    p.block_size_log2 = log2_int(block_size);
+    p.max_context_len = max_context_len;
+    p.top_k = top_k;
+    // Waves of the score kernel: enough to fill the chip (8 per compute unit), at most one per unit.
+    const int64_t units_max = (int64_t)num_seqs * ((max_context_len + 15) / 16);
+    const int64_t waves = std::max<int64_t>(4, std::min<int64_t>((int64_t)device_cus() * 8, units_max));
+    p.num_waves = (int32_t)((waves + 3) / 4 * 4);
+    return hip_status(pa::launch_indexer_topk(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -66,6 +66,8 @@ __shared__ __attribute__((aligned(16))) char s_raw3[kRawStage];
 __shared__ __attribute__((aligned(16))) char s_junk[1024];  // target of loads past the last window
 __shared__ __attribute__((aligned(16))) char s_tile0[kTileStage];
 __shared__ __attribute__((aligned(16))) char s_tile1[kTileStage];
+// Sparse form: the slots of unit g (32 used of 64 entries) in table g % 8, copied four units ahead.
+__shared__ __attribute__((aligned(16))) int32_t s_slot[8][64];
 
 template <int K>
 __device__ __forceinline__ char* raw_stage() {
@@ -88,7 +90,8 @@ __device__ __forceinline__ char* tile_stage() {
 __device__ __forceinline__ int swz(int r) { return (((r >> 2) & 3) << 1) | (r & 1); }
 
 __device__ __forceinline__ int clamp_ctx(int64_t ctx, const MlaDecodeParams& p) {
-    const int64_t cap = min((int64_t)p.max_context_len, (int64_t)p.bt_stride * p.block_size);
+    const int64_t row = p.slots != nullptr ? p.slot_stride : (int64_t)p.bt_stride * p.block_size;
+    const int64_t cap = min((int64_t)p.max_context_len, row);
     return (int)max((int64_t)0, min(ctx, cap));
 }
 
@@ -182,10 +185,16 @@ __device__ __forceinline__ uint4 dequant8(uint2 b, float sc) {
 // NW: waves per work-group; each wave owns 16 heads (heads_per_wg = 16 * NW). With 8 waves (128
 // heads) two waves share each SIMD, so one wave's vector and LDS work overlaps the other's MFMAs;
 // that caps a wave at 256 registers: 128 accumulators for its 16 x 512 output, 72 for its queries.
-template <int NW>
+//
+// SPARSE: token i of sequence s is the row at slot slots[s][i], in any block. The slots of a unit are
+// copied into LDS (s_slot) along with the rows of the unit four places earlier, so each lane finds
+// the row of each of its 16-byte chunks there when it issues the unit's copy; a row whose slot is
+// outside the pool, or past the sequence's count, is read from q and masked out.
+template <int NW, bool SPARSE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 4 ? 2 : 1, NW > 4 ? 2 : 1)))
 void decode_mla_kernel(MlaDecodeParams p) {
-    constexpr int R = (kWindows + NW - 1) / NW;  // load instructions per lane per unit
+    constexpr int R = (kWindows + NW - 1) / NW;  // row-copy instructions per lane per unit
+    constexpr int RL = R + (SPARSE ? 1 : 0);     // all copy instructions per lane per unit
     constexpr int kLatentIters = kUnit / NW;     // tile rows each wave dequantizes per unit
     constexpr int kRopeIters = (kRopeChunks + 64 * NW - 1) / (64 * NW);
     constexpr int kDimTiles = 32;                // 512 value dims in 16-dim output tiles
@@ -234,12 +243,12 @@ void decode_mla_kernel(MlaDecodeParams p) {
     uint4 qr[kKSteps];
     f32x4_t O[kDimTiles];  // register j of lane (c, g4): head 4 g4 + j, dim 16 dt + c
     float m = kNegInf, l = 0.f;
-    // Unit validity, one slot per raw stage: bits 0..7 valid rows, bit 8 / 9 rows 0..15 / 16..31 in a
-    // valid block.
-    int info[4];
+    // Unit validity, one mask per raw stage: bit r set when row r holds a token of the unit.
+    uint32_t info[4];
 
     Cursor cc = locate(g_begin, p, lane);  // unit being computed
     Cursor cl = cc;                        // next unit to load
+    Cursor cs = cc;                        // sparse: next unit whose slot table is copied
     bool seg_from_start = false;           // the current segment began at the sequence's first unit
 
     // Empty asm statements that tie the queries to vector registers and the outputs to accumulation
@@ -272,7 +281,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
     // is hidden (pre_pb: rows 16..31 when block_size is 16).
     int pre_pa = 0, pre_pb = 0;
     auto prefetch_ids = [&]() __attribute__((always_inline)) {
-        if (cl.g < g_end) {
+        if (!SPARSE && cl.g < g_end) {
             const int t0 = cl.k * kUnit;
             const int32_t* bt = p.block_tables + (int64_t)cl.s * p.bt_stride;
             const int lb = t0 >> p.block_size_log2;
@@ -283,8 +292,50 @@ void decode_mla_kernel(MlaDecodeParams p) {
 
     // Copies unit cl into raw stage K, records its validity in info[K], advances cl and prefetches the
     // next unit's block ids.
+    // Slot table of unit cs: wave 0 copies 64 entries (the unit's 32, then the next 32, clamped to the
+    // sequence) into s_slot[cs.g % 8]; the other waves issue the same instruction into s_junk, so that
+    // every wave counts RL copies per unit.
+    auto copy_slot_table = [&]() __attribute__((always_inline)) {
+        const int32_t* src = p.slots;
+        if (cs.g < g_end) src = p.slots + (int64_t)cs.s * p.slot_stride + min(cs.k * kUnit + lane, cs.ctx - 1);
+        void* dst = wave == 0 ? static_cast<void*>(s_slot[cs.g & 7]) : static_cast<void*>(s_junk);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+        advance(cs, p);
+    };
+
+    auto issue_sparse = [&](auto kst) __attribute__((always_inline)) {
+        constexpr int K = decltype(kst)::value;
+        const int v = cl.g < g_end ? min(kUnit, cl.ctx - cl.k * kUnit) : 0;
+        const int32_t* tab = s_slot[cl.g & 7];
+        const uint32_t nslots = (uint32_t)p.num_slots;
+        const int32_t mine = tab[lane & 31];
+        info[K] = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && lane < v && (uint32_t)mine < nslots);
+        char* stage = raw_stage<K>();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int win = r * NW + wave;
+            const int kk = dma_kk[r];
+            const int row = kk / 41;  // >= 32 past the unit's last chunk
+            const int32_t sl = tab[row & 31];
+            const bool ok = row < v && (uint32_t)sl < nslots;
+            const char* src = ok ? p.kv + (int64_t)(sl >> p.block_size_log2) * p.block_stride +
+                                       (int64_t)(sl & (p.block_size - 1)) * kRow + (kk - row * 41) * 16
+                                 : dummy;
+            char* dst = win < kWindows ? stage + win * 1024 : s_junk;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        }
+        copy_slot_table();
+        advance(cl, p);
+    };
+
     auto issue = [&](auto kst) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
+        if constexpr (SPARSE) {
+            issue_sparse(kst);
+            return;
+        }
         const bool live = cl.g < g_end;
         int v = 0;
         const char* base_a = dummy;              // rows 0..15 (all rows when block_size >= 32)
@@ -317,7 +368,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
                 }
             }
         }
-        info[K] = v | (ok_a ? 0x100 : 0) | (ok_b ? 0x200 : 0);
+        info[K] = (v >= 32 ? 0xFFFFFFFFu : (1u << v) - 1u) & ((ok_a ? 0xFFFFu : 0u) | (ok_b ? 0xFFFF0000u : 0u));
         char* stage = raw_stage<K>();
         const bool split = p.block_size < kUnit;
 #pragma unroll
@@ -353,22 +404,20 @@ void decode_mla_kernel(MlaDecodeParams p) {
             in.sc[it] = *reinterpret_cast<const float*>(raw + conv_scale + it * NW * kRow);
         }
     };
-    auto conv_store = [&](auto kr, auto kt, int vi, const ConvIn& in, int i0, auto cnt, bool rope)
+    auto conv_store = [&](auto kr, auto kt, uint32_t vmask, const ConvIn& in, int i0, auto cnt, bool rope)
         __attribute__((always_inline)) {
         constexpr int KR = decltype(kr)::value;
         constexpr int KT = decltype(kt)::value;
         constexpr int CNT = decltype(cnt)::value;
         const char* raw = raw_stage<KR>();
         char* tile = tile_stage<KT>();
-        const int v = vi & 0xFF;
-        const bool ok_a = vi & 0x100, ok_b = vi & 0x200;
 #pragma unroll
         for (int jj = 0; jj < CNT; ++jj) {
             const int it = i0 + jj;
             if (it < kLatentIters) {
                 const int r = it * NW + wave;  // wave-uniform
                 const uint4 d = dequant8(in.b8[it], in.sc[it]);
-                const bool keep = r < v && (r < 16 ? ok_a : ok_b);
+                const bool keep = (vmask >> r) & 1u;
                 *reinterpret_cast<uint4*>(tile + r * kTileRow + ((lane ^ swz(r)) << 4)) =
                     keep ? d : make_uint4(0u, 0u, 0u, 0u);
             }
@@ -380,7 +429,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
                 if (kRopeChunks % (64 * NW) == 0 || n < kRopeChunks) {
                     const int r = n >> 3, k8 = n & 7;
                     const uint4 d = *reinterpret_cast<const uint4*>(raw + r * kRow + kRopeOff + 16 * k8);
-                    const bool keep = r < v && (r < 16 ? ok_a : ok_b);
+                    const bool keep = (vmask >> r) & 1u;
                     *reinterpret_cast<uint4*>(tile + r * kTileRow + ((64 + (k8 ^ swz(r))) << 4)) =
                         keep ? d : make_uint4(0u, 0u, 0u, 0u);
                 }
@@ -466,11 +515,9 @@ void decode_mla_kernel(MlaDecodeParams p) {
     // PV slots. Each slot loads the next slot's LDS operands, then issues its own products; the
     // scheduling barriers keep the compiler from hoisting every operand load to the top, which would
     // need more registers than the queries and outputs leave free.
-    auto compute = [&](auto kt, int vi, auto kr2, auto kt2, int vn) __attribute__((always_inline)) {
+    auto compute = [&](auto kt, uint32_t vmask, auto kr2, auto kt2, uint32_t vn) __attribute__((always_inline)) {
         constexpr int KT = decltype(kt)::value;
         const char* tile = tile_stage<KT>();
-        const int v = vi & 0xFF;
-        const bool ok_a = vi & 0x100, ok_b = vi & 0x200;
         const int g4 = lane >> 4;
 
         // The dequantization of the next unit starts with its LDS reads, whose results are used
@@ -502,7 +549,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ok[t][j] = 16 * t + g4 + 4 * j < v && (t == 0 ? ok_a : ok_b);
+            for (int j = 0; j < 4; ++j) ok[t][j] = (vmask >> (16 * t + g4 + 4 * j)) & 1u;
         float mx = kNegInf;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -572,12 +619,12 @@ void decode_mla_kernel(MlaDecodeParams p) {
     // while dequantizing unit u+1. Returns false when the range is done.
     auto step = [&](auto kst) __attribute__((always_inline)) -> bool {
         constexpr int K = decltype(kst)::value;
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * R));  // own loads of unit u+1 are done
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * RL));  // own loads of unit u+1 are done
         compiler_fence();
         __builtin_amdgcn_s_barrier();                          // everyone's are; step u-1 is finished
         compiler_fence();
-        const int cur = info[K];
-        const int nxt = info[(K + 1) & 3];
+        const uint32_t cur = info[K];
+        const uint32_t nxt = info[(K + 1) & 3];
         pin_queries();
         pin_outputs();
         refresh_offsets();
@@ -590,13 +637,20 @@ void decode_mla_kernel(MlaDecodeParams p) {
         return cc.g < g_end;
     };
 
-    // Prologue: units 0..3 in flight, unit 0 dequantized.
+    // Prologue: units 0..3 in flight, unit 0 dequantized. The sparse form first copies the slot
+    // tables of units 0..3 and waits for them.
+    if constexpr (SPARSE) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) copy_slot_table();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        lds_barrier();
+    }
     prefetch_ids();
     issue(std::integral_constant<int, 0>{});
     issue(std::integral_constant<int, 1>{});
     issue(std::integral_constant<int, 2>{});
     issue(std::integral_constant<int, 3>{});
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * R));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * RL));
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
@@ -644,7 +698,10 @@ namespace {
 template <int NW>
 hipError_t launch_mla_typed(const MlaDecodeParams& p, hipStream_t stream) {
     const dim3 grid((unsigned)p.num_wgs, (unsigned)(p.num_q_heads / p.heads_per_wg));
-    hipLaunchKernelGGL((decode_mla_kernel<NW>), grid, dim3(64 * NW), 0, stream, p);
+    if (p.slots != nullptr)
+        hipLaunchKernelGGL((decode_mla_kernel<NW, true>), grid, dim3(64 * NW), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_mla_kernel<NW, false>), grid, dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -141,8 +141,41 @@ struct MlaDecodeParams {
     int32_t num_wgs;           // work-groups along x
     int32_t units_per_wg;      // 0: balanced over num_wgs
     float scale_log2;          // softmax scale * log2(e)
+    // Sparse form: token i of sequence s is the row at slot slots[s * slot_stride + i] (block =
+    // slot >> block_size_log2, position = slot & (block_size - 1)); context_lens holds the number of
+    // slots and block_tables is unused. A slot outside [0, num_slots) contributes no token.
+    const int32_t* slots;      // nullptr: the dense form, through block_tables
+    int64_t slot_stride;
+    int64_t num_slots;
 };
 hipError_t launch_decode_mla(const MlaDecodeParams& p, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// DSA indexer: scores of every context token from the indexer rows, then each sequence's top-k
+// ---------------------------------------------------------------------------
+struct IndexerParams {
+    const char* idx;           // cache base + view offset + layer * layer_stride (132-byte rows)
+    const uint16_t* q;         // bf16 [num_seqs, num_heads, 128]
+    const float* w;            // [num_seqs, num_heads]
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* scores;             // [num_seqs, score_stride]
+    int32_t* topk_pos;         // [num_seqs, top_k]
+    int32_t* topk_slots;       // [num_seqs, top_k]
+    int32_t* topk_lens;        // [num_seqs]
+    int64_t score_stride;
+    int64_t block_stride;
+    int64_t num_blocks;
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t num_heads;         // 16, 32, 48 or 64
+    int32_t block_size;
+    int32_t block_size_log2;
+    int32_t max_context_len;   // clamp for context_lens
+    int32_t num_waves;         // waves of the score kernel's grid
+    int32_t top_k;
+};
+hipError_t launch_indexer_topk(const IndexerParams& p, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Causal chunks over paged context (query length >= 2), head_dim 128, group 1..16

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
-    assert pa.abi_version() == 2
+    assert pa.abi_version() == 3
 
 
 def test_status_strings():
@@ -212,3 +212,60 @@ def test_fp8_status_codes():
     g16 = pa.dense_desc("fp8", 32, 2, 64, 16, 64, 64 * 16 * 128, 64 * 16 * 128, k_scale=0.5, v_scale=0.5)
     assert decode(g16) == E.PA_ERR_UNSUPPORTED                           # group 16 needs head_dim 128
     assert pa.pa_decode_workspace_bytes(d, 4, 2048) > 0
+
+
+def topk(pos=FAKE, slots=FAKE, lens=FAKE, k=2048, scores=FAKE, ss=8192, q=FAKE, w=FAKE, H=64, ic=FAKE,
+         ib=9216 * 100864, iview=None, layer=1, bt=FAKE, bts=128, ctx=FAKE, B=64, max_ctx=8192, bs=64, nb=9216):
+    iview = iview or pa.CacheView(83968, 8448, 100864, 132).c()
+    return L._lib.pa_indexer_topk(pos, slots, lens, k, scores, ss, q, w, H, ic, ib, iview, layer, bt, bts, ctx, B,
+                                  max_ctx, bs, nb, None)
+
+
+def test_indexer_topk_status_codes():
+    E = L
+    assert topk(B=0) == E.PA_OK                                     # no-op, nothing enqueued
+    assert topk(B=-1) == E.PA_ERR_INVALID_ARGUMENT
+    assert topk(scores=None) == E.PA_ERR_NULL_POINTER
+    assert topk(slots=None) == E.PA_ERR_NULL_POINTER
+    assert topk(k=0) == E.PA_ERR_INVALID_ARGUMENT
+    assert topk(ss=8191) == E.PA_ERR_INVALID_ARGUMENT               # score row shorter than the context
+    assert topk(H=40) == E.PA_ERR_UNSUPPORTED                       # heads in tiles of 16, at most 64
+    assert topk(H=80) == E.PA_ERR_UNSUPPORTED
+    assert topk(bs=48) == E.PA_ERR_UNSUPPORTED
+    assert topk(iview=pa.CacheView(83968, 8448, 100864, 128).c()) == E.PA_ERR_INVALID_ARGUMENT  # not 132
+    assert topk(ib=9216 * 100864 - 1) == E.PA_ERR_VIEW_OUT_OF_RANGE
+    assert topk(nb=1 << 26, ib=1 << 62) == E.PA_ERR_UNSUPPORTED     # slots would not fit in int32
+    assert topk(q=FAKE + 4) == E.PA_ERR_MISALIGNED
+    assert topk(iview=pa.CacheView(83970, 8448, 100864, 132).c(), ib=9216 * 100864 + 16) == E.PA_ERR_MISALIGNED
+
+
+def mla_desc(**kw):
+    d = pa.AttnDesc(kv_format=L.PA_KV_MLA656_E4M3, num_q_heads=128, num_kv_heads=1, qk_dim=576, v_dim=512,
+                    block_size=64, layer=1, num_blocks=9216, k_view=pa.CacheView(0, 41984, 100864, 656),
+                    v_view=pa.CacheView(0, 41984, 100864, 656), k_cache_bytes=9216 * 100864, v_cache_bytes=0)
+    for key, v in kw.items():
+        setattr(d, key, v)
+    return d
+
+
+def sparse(desc, out=FAKE, q=FAKE, kv=FAKE, slots=FAKE, stride=2048, counts=FAKE, B=64, max_count=2048, scale=0.04,
+           ws=None, ws_bytes=0):
+    d = desc.c() if desc is not None else None
+    return L._lib.pa_mla_sparse_decode(out, q, kv, slots, stride, counts, B, max_count, scale,
+                                       ctypes.byref(d) if d is not None else None, ws, ws_bytes, None)
+
+
+def test_mla_sparse_decode_status_codes():
+    E = L
+    assert sparse(None) == E.PA_ERR_NULL_POINTER
+    assert sparse(mla_desc(), B=0) == E.PA_OK
+    assert sparse(mla_desc(), B=-2) == E.PA_ERR_INVALID_ARGUMENT
+    assert sparse(mla_desc(), slots=None) == E.PA_ERR_NULL_POINTER
+    assert sparse(mla_desc(), stride=0) == E.PA_ERR_INVALID_ARGUMENT
+    assert sparse(mla_desc(), scale=float("inf")) == E.PA_ERR_INVALID_ARGUMENT
+    assert sparse(mla_desc(kv_format=L.PA_KV_BF16)) == E.PA_ERR_UNSUPPORTED
+    assert sparse(mla_desc(num_q_heads=24)) == E.PA_ERR_UNSUPPORTED
+    assert sparse(mla_desc(k_cache_bytes=100)) == E.PA_ERR_VIEW_OUT_OF_RANGE
+    assert sparse(mla_desc(), slots=FAKE + 2) == E.PA_ERR_MISALIGNED
+    assert sparse(mla_desc(), ws=None, ws_bytes=0) == E.PA_ERR_WORKSPACE
+

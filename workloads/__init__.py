@@ -25,7 +25,10 @@ Workload recipes. Each one stands in for a workload the pages describe:
 * ``dsa_mla``: the DSA dual cache in block-outer BLHNC layout. 2 layers,
   block size 64, 656-byte MLA rows and 132-byte indexer rows, then MLA decode
   with 128 heads on one latent head. The layout is the worked example of the
-  "vLLM KV Cache Layout 可视化" page.
+  "vLLM KV Cache Layout 可视化" page. The sparse path adds, per decode token, 64
+  lightning-indexer queries of 128 bf16 values with float32 head weights
+  N(0, 1/64), and selects the top 2048 tokens (the page gives neither the head
+  count nor k; these are DeepSeek's published indexer settings).
 
 Every draw uses NumPy's PCG64 with a fixed seed per workload. Values are
 N(0, 1) float32, rounded to the storage type with round-to-nearest-even by
@@ -44,6 +47,7 @@ from .gen import (  # noqa: F401
     draw_context_lens,
     draw_mla_rows,
     draw_indexer_rows,
+    draw_index_queries,
     f16_nan_bits,
     bf16_nan_bits,
     make_dense_case,

@@ -31,7 +31,8 @@ WORKLOADS = {
                        block_size=16, num_blocks=17408),
     "dsa_mla": dict(num_layers=2, block_size=64, num_blocks=9216, mla_row_bytes=656,
                     indexer_row_bytes=132, num_seqs=64, ctx_low=1024, ctx_high=8192,
-                    num_q_heads=128, latent_dim=512, rope_dim=64, scale_group=128),
+                    num_q_heads=128, latent_dim=512, rope_dim=64, scale_group=128,
+                    index_heads=64, index_dim=128, top_k=2048),
 }
 
 
@@ -375,6 +376,17 @@ def draw_indexer_rows(seed: int, n: int, device: str = "cpu"):
     return rows
 
 
+def draw_index_queries(seed: int, num_seqs: int, num_heads: int, device: str = "cpu"):
+    """Lightning-indexer inputs of num_seqs decode tokens: queries as bf16 bits (torch int16
+    [B, H, 128], N(0, 1)) and head weights (torch float32 [B, H], N(0, 1 / H))."""
+    torch = _torch()
+    q = draw_bits(seed, (num_seqs, num_heads, 128), "bf16", device)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) + 1)
+    w = torch.randn(num_seqs, num_heads, generator=g, device=device, dtype=torch.float32) / math.sqrt(num_heads)
+    return q, w
+
+
 @dataclass
 class MlaCase:
     num_layers: int
@@ -393,6 +405,10 @@ class MlaCase:
     idx_rows: list = field(default_factory=list)      # per layer: uint8 [N, 132]
     step_mla_rows: list = field(default_factory=list)  # per layer: uint8 [B, 656]
     step_idx_rows: list = field(default_factory=list)  # per layer: uint8 [B, 132]
+    index_heads: int = 64
+    top_k: int = 2048
+    q_index: object = None          # torch int16 [B, index_heads, 128] bf16 bits
+    index_weights: object = None    # torch float32 [B, index_heads]
 
 
 def make_mla_case(device: str = "cpu", seed: int | None = None, context_lens=None,
@@ -428,4 +444,6 @@ def make_mla_case(device: str = "cpu", seed: int | None = None, context_lens=Non
             case.idx_rows.append(draw_indexer_rows(seed * 16 + 6 + 4 * layer, len(pop), device))
             case.step_mla_rows.append(draw_mla_rows(seed * 16 + 7 + 4 * layer, B, device))
             case.step_idx_rows.append(draw_indexer_rows(seed * 16 + 8 + 4 * layer, B, device))
+        case.index_heads, case.top_k = p["index_heads"], p["top_k"]
+        case.q_index, case.index_weights = draw_index_queries(seed * 16 + 13, B, p["index_heads"], device)
     return case

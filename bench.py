@@ -12,7 +12,8 @@ the pa_decode call (the dominant kernel): its algorithmic bytes over its own dur
 recorded around every call on the launch stream. `cpu_baseline` times the NumPy oracle on the host
 cores over a bounded sample of the same batch. `extra` holds short runs of the other workloads, each
 measured the same way: GQA-8 with a shared or copied 2000-token prompt, long-context decode,
-the mixed chunked-prefill steps, and the DSA dual-cache write plus MLA decode.
+the mixed chunked-prefill steps, the DSA dual-cache write plus MLA decode, and the DSA sparse step
+(indexer scores, top-k, MLA decode over the selected slots).
 """
 
 from __future__ import annotations
@@ -32,7 +33,7 @@ FP8_SCALE = 2.0 ** -5       # K and V scale of the FP8 cache variants (N(0,1) va
 MFMA_BF16_PEAK_TF = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = ("api.hip", "cache_write.hip", "decode_dense.hip", "decode_fp8.hip", "decode_mfma.hip", "decode_mla.hip",
-                  "prefill_mfma.hip", "decode_common.h", "decode_mfma.h", "mfma_common.h", "pa_device.h", "pa_internal.h")
+                  "dsa_indexer.hip", "prefill_mfma.hip", "decode_common.h", "decode_mfma.h", "mfma_common.h", "pa_device.h", "pa_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -382,6 +383,7 @@ def run_mla(steps, warmup):
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
     dec_ms = float(np.mean(tms[0].ms() + tms[1].ms()))
+    sparse = run_dsa_sparse(case, img, idx_v, descs, tables, lens, steps, warmup)
     sum_ctx = int(case.context_lens.sum())
     kv = sum_ctx * 656 + B * 128 * 576 * 2 + B * 128 * 512 * 2 + int(((case.context_lens + bs - 1) // bs).sum()) * 4
     flops = sum_ctx * 128 * (576 + 512) * 2
@@ -403,6 +405,72 @@ def run_mla(steps, warmup):
                      "kernel": "pa_decode (decode_mla_kernel + mla_merge_kernel)",
                      "algorithmic_flops_per_call": flops, "algorithmic_bytes_per_call": kv},
         "sum_context_tokens": sum_ctx,
+        "sparse": sparse,
+    }
+
+
+def run_dsa_sparse(case, img, idx_v, descs, tables, lens, steps, warmup):
+    """DSA sparse step per layer: indexer scores + top-k (pa_indexer_topk), then MLA decode over the selection."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_130_amd as pa
+    B, H, K = len(case.context_lens), case.index_heads, case.top_k
+    max_ctx = int(case.context_lens.max())
+    stream = torch.cuda.current_stream()
+    scores = torch.empty(B, max_ctx, dtype=torch.float32, device="cuda")
+    pos = torch.empty(B, K, dtype=torch.int32, device="cuda")
+    slots = torch.empty_like(pos)
+    counts = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(16, pa.pa_decode_workspace_bytes(descs[0], B, K)), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, case.num_q_heads, 512, dtype=torch.int16, device="cuda")
+
+    def step(ti=None, td=None, i=0):
+        for layer in range(2):
+            if ti is not None:
+                ti[layer].ev[i][0].record(stream)
+            pa.pa_indexer_topk(pos, slots, counts, scores, case.q_index, case.index_weights, img, idx_v, layer,
+                               tables, lens, max_ctx, case.block_size, case.num_blocks)
+            if ti is not None:
+                ti[layer].ev[i][1].record(stream)
+                td[layer].ev[i][0].record(stream)
+            pa.pa_mla_sparse_decode(out, case.q, img, slots, counts, K, case.scale, descs[layer], ws)
+            if td is not None:
+                td[layer].ev[i][1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    ti, td = [Timer(torch, steps), Timer(torch, steps)], [Timer(torch, steps), Timer(torch, steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ti, td, i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    idx_ms = float(np.mean(ti[0].ms() + ti[1].ms()))
+    dec_ms = float(np.mean(td[0].ms() + td[1].ms()))
+    ctx = case.context_lens.astype(np.int64)
+    sel = np.minimum(ctx, K)
+    nblk = int(((ctx + case.block_size - 1) // case.block_size).sum())
+    # Indexer call: index rows read once, queries and weights, table entries; scores written then re-read
+    # by the selection; positions and slots written.
+    idx_bytes = int(ctx.sum()) * (132 + 4 + 4) + B * H * (128 * 2 + 4) + nblk * 4 + B * K * 8
+    dec_bytes = int(sel.sum()) * (656 + 4) + B * 128 * (576 + 512) * 2
+    dec_flops = int(sel.sum()) * 128 * (576 + 512) * 2
+    tf = dec_flops / (dec_ms / 1e3) / 1e12
+    return {
+        "workload": (f"DSA sparse decode on the same cache, per layer: lightning indexer ({H} heads x 128, bf16 "
+                     f"queries, fp8 keys) over every context token, top {K} per sequence, MLA decode over the "
+                     "selected slots"),
+        "ms_per_step_two_layers": ms_step,
+        "decode_tokens_per_s": B / (ms_step / 1e3),
+        "indexer_topk_call_ms": idx_ms,
+        "indexer_topk_gbs": idx_bytes / (idx_ms / 1e3) / 1e9,
+        "indexer_topk_hbm_frac": idx_bytes / (idx_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "sparse_decode_call_ms": dec_ms,
+        "sparse_decode_tflops": tf,
+        "sparse_decode_mfma_frac": tf / MFMA_BF16_PEAK_TF,
+        "sparse_decode_gbs": dec_bytes / (dec_ms / 1e3) / 1e9,
+        "selected_tokens": int(sel.sum()),
     }
 
 
@@ -528,6 +596,7 @@ def main():
                                               "mla_hbm_frac")}
         extra["dsa_mla"]["mfma_tflops"] = m["roofline"]["achieved"]
         extra["dsa_mla"]["mfma_frac"] = m["roofline"]["frac"]
+        extra["dsa_sparse"] = m["sparse"]
         res["extra"] = extra
     print(json.dumps(rounded(res)), flush=True)
 

@@ -313,7 +313,8 @@ int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const vo
  *   index_cache, index_cache_bytes, index_view, layer  the indexer view (row_bytes 132).
  *   block_tables, bt_stride, context_lens, max_context_len, block_size, num_blocks  as for pa_decode.
  * num_blocks * block_size must fit in int32. Scores are unspecified for non-finite inputs or a
- * negative scale (memory-safe). Alignment: q_index 16 bytes; everything else 4 bytes.
+ * negative scale (memory-safe). Alignment: q_index, index_cache, the view's offset, block_stride
+ * and layer * layer_stride 16 bytes; everything else 4 bytes.
  * num_seqs == 0 is a no-op. */
 int32_t pa_indexer_topk(int32_t* topk_positions, int32_t* topk_slots, int32_t* topk_lens, int32_t top_k,
                         float* scores, int64_t score_stride, const void* q_index, const float* head_weights,

@@ -624,7 +624,9 @@ int32_t pa_indexer_topk(int32_t* topk_positions, int32_t* topk_slots, int32_t* t
     if (st != PA_OK) return st;
     if (num_blocks * block_size > 0x7FFFFFFFLL) return PA_ERR_UNSUPPORTED;  // slots are int32
     if ((int64_t)num_seqs * top_k > 0x7FFFFFFFLL || (int64_t)num_seqs > 0x7FFFFFFFLL / 64) return PA_ERR_UNSUPPORTED;
-    if (!aligned(q_index, 16) || !aligned(index_cache, 4) || !view_aligned(index_view, layer, 4) ||
+    if (!aligned(q_index, 16) || !aligned(index_cache, 16) || !view_aligned(index_view, layer, 4) ||
+        !aligned(index_view.offset, 16) || !aligned((int64_t)layer * index_view.layer_stride, 16) ||
+        !aligned(index_view.block_stride, 16) ||
         !aligned(head_weights, 4) || !aligned(scores, 4) || !aligned(topk_positions, 4) ||
         !aligned(topk_slots, 4) || !aligned(topk_lens, 4) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return PA_ERR_MISALIGNED;
@@ -649,10 +651,7 @@ int32_t pa_indexer_topk(int32_t* topk_positions, int32_t* topk_slots, int32_t* t
     p.block_size_log2 = log2_int(block_size);
     p.max_context_len = max_context_len;
     p.top_k = top_k;
-    // Waves of the score kernel: enough to fill the chip (8 per compute unit), at most one per unit.
-    const int64_t units_max = (int64_t)num_seqs * ((max_context_len + 15) / 16);
-    const int64_t waves = std::max<int64_t>(4, std::min<int64_t>((int64_t)device_cus() * 8, units_max));
-    p.num_waves = (int32_t)((waves + 3) / 4 * 4);
+    if ((int64_t)num_seqs * ((max_context_len + 511) / 512) > 0x7FFFFFFFLL) return PA_ERR_UNSUPPORTED;
     return hip_status(pa::launch_indexer_topk(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -13,14 +13,17 @@
 // Scores. q_j . codes_t for 16 tokens and all H heads is a (16 x 128) by (128 x H) product: it runs
 // on v_mfma_f32_16x16x32_bf16, with the e4m3 codes widened exactly to bf16 by the gfx950 convert.
 // Per token the kernel reads 132 bytes and does 256 H flops (H = 64: about 124 flop per byte, under
-// the bf16 ridge of about 310), so it is bound by HBM. A wave holds one sequence's queries (four
-// 16-byte operands per 16 heads) and streams a balanced range of the 16-token units of all sequences,
-// three units in flight.
+// the bf16 ridge of about 310), so it is bound by HBM. A work-group takes 512 consecutive tokens of
+// one sequence: its four waves share the sequence's queries through LDS (read once from memory) and
+// hold them in registers; each wave loads its 128 tokens' rows as eight flat, coalesced 2112-byte
+// runs (16 rows each), all in flight at once, and stages each run through LDS to pick out the MFMA
+// operands (rows are 132 bytes, so a row's bytes do not line up with the lanes of a flat load).
 //
 // Top-k. One work-group per sequence finds the k-th largest score by a radix select over
-// order-preserving 32-bit keys (four 8-bit digit passes, per-wave histograms in LDS), then writes
-// the selected positions in ascending order through a work-group prefix scan, taking the scores tied
-// at the threshold from the earliest positions, and each position's slot through the block table.
+// order-preserving 32-bit keys (three 11/11/10-bit digit passes over a histogram in LDS), then
+// writes the selected positions in ascending order through one work-group prefix scan per 8192
+// positions, taking the scores tied at the threshold from the earliest positions, and each
+// position's slot through the block table.
 
 #include "decode_common.h"
 #include "mfma_common.h"
@@ -29,17 +32,15 @@ namespace pa {
 
 namespace {
 
-constexpr int kIdxRow = 132;   // 128 e4m3 key values + 1 float32 scale
-constexpr int kIdxUnit = 16;   // tokens per unit: the rows of one MFMA tile
-constexpr int kDepth = 3;      // units in flight per wave
+constexpr int kIdxRow = 132;                    // 128 e4m3 key values + 1 float32 scale
+constexpr int kIdxUnit = 16;                    // tokens per unit: the rows of one MFMA tile
+constexpr int kUnitBytes = kIdxUnit * kIdxRow;  // 2112 = 132 chunks of 16 bytes
+constexpr int kUnitChunks = kUnitBytes / 16;
+constexpr int kWaveUnits = 8;                   // units per wave (128 tokens)
+constexpr int kWgTokens = 4 * kWaveUnits * kIdxUnit;  // 512 tokens per work-group
+constexpr int kQRow = 128 * 2 + 16;             // LDS row of one query head (padded against conflicts)
 
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-
-// Rows are 132 bytes, so their 16-byte pieces are only 4-byte aligned.
-__device__ __forceinline__ uint4 load16_a4(const char* ptr) {
-    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(ptr);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 // Two e4m3 codes (bytes 0, 1 or 2, 3 of w) -> two bf16 (exact: every e4m3 value is a bf16 value).
 template <bool HI>
@@ -59,189 +60,116 @@ __device__ __forceinline__ int idx_ctx(int64_t ctx, const IndexerParams& p) {
     return (int)max((int64_t)0, min(ctx, cap));
 }
 
-__device__ __forceinline__ int idx_units(int ctx) { return (ctx + kIdxUnit - 1) / kIdxUnit; }
-
-// Position in the stream of 16-token units of all sequences (wave-uniform).
-struct IdxCursor {
-    int g;    // unit index in the stream
-    int s;    // sequence
-    int k;    // unit within the sequence
-    int nu;   // units of the sequence
-    int ctx;  // tokens of the sequence
-};
-
-__device__ __forceinline__ void idx_advance(IdxCursor& c, const IndexerParams& p) {
-    ++c.g;
-    if (++c.k < c.nu) return;
-    c.k = 0;
-    do {
-        ++c.s;
-        c.ctx = c.s < p.num_seqs ? idx_ctx(load_scalar(p.context_lens + c.s), p) : 0;
-        c.nu = idx_units(c.ctx);
-    } while (c.nu == 0 && c.s < p.num_seqs);
-}
-
-__device__ int idx_total_units(const IndexerParams& p, int lane) {
-    int u = 0;
-    for (int base = 0; base < p.num_seqs; base += 64) {
-        const int s = base + lane;
-        int v = s < p.num_seqs ? idx_units(idx_ctx(p.context_lens[s], p)) : 0;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        u += v;
-    }
-    return __builtin_amdgcn_readfirstlane(u);
-}
-
-// Cursor of unit g0 (g0 < total units).
-__device__ IdxCursor idx_locate(int g0, const IndexerParams& p, int lane) {
-    int before = 0;
-    for (int base = 0; base < p.num_seqs; base += 64) {
-        const int s = base + lane;
-        const int ctx = s < p.num_seqs ? idx_ctx(p.context_lens[s], p) : 0;
-        const int nu = idx_units(ctx);
-        int incl = nu;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl(incl, max(lane - off, 0));
-            if (lane >= off) incl += t;
-        }
-        const int total = __builtin_amdgcn_readlane(incl, 63);
-        if (g0 < before + total) {
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(before + incl > g0);
-            const int ls = __builtin_ctzll(hit);
-            IdxCursor c;
-            c.g = g0;
-            c.s = base + ls;
-            c.ctx = __builtin_amdgcn_readlane(ctx, ls);
-            c.nu = __builtin_amdgcn_readlane(nu, ls);
-            c.k = g0 - (before + __builtin_amdgcn_readlane(incl, ls) - c.nu);
-            return c;
-        }
-        before += total;
-    }
-    IdxCursor c{g0, p.num_seqs, 0, 0, 0};
-    return c;
-}
-
-// One unit's rows as a lane holds them: lane (c, g4) = (lane % 16, lane / 16) has bytes
-// [16 g4, 16 g4 + 16) and [64 + 16 g4, 64 + 16 g4 + 16) of row c, and the scale of row 4 g4 + (c & 3),
-// the token whose score it writes.
-struct RawUnit {
-    uint4 a, b;
-    float sc;
-    int ok;  // the unit's block id is valid (wave-uniform)
-};
-
 }  // namespace
 
-// HT = H / 16 head tiles. Product layout: A = key codes (row = token c), B = queries (column = head
-// c of the tile), both with the k slots of lane group g4 at dims {16 g4 .. 16 g4 + 15} (k steps 0, 1)
-// and {64 + 16 g4 ..} (k steps 2, 3); output register j of lane (c, g4) is token 4 g4 + j, head c.
+// Grid: ceil(max_context_len / 512) work-groups per sequence. HT = H / 16 head tiles. Product layout:
+// A = queries (row = head c of the tile), B = key codes (column = token c), both with the k slots of
+// lane group g4 at dims {16 g4 .. 16 g4 + 15} (k steps 0, 1) and {64 + 16 g4 ..} (k steps 2, 3);
+// output register j of lane (c, g4) is head 16 ht + 4 g4 + j, token c. A lane weighs and sums its 16
+// heads, two cross-lane steps add the four lane groups, and lanes 0..15 write tokens 0..15.
 template <int HT>
-__global__ __launch_bounds__(256) void indexer_score_kernel(IndexerParams p) {
-    const int lane = threadIdx.x & 63;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void indexer_score_kernel(IndexerParams p) {
+    __shared__ __attribute__((aligned(16))) char s_q[HT * 16 * kQRow];
+    __shared__ float s_w[HT * 16];
+    __shared__ __attribute__((aligned(16))) char s_stage[4][2][3 * 64 * 16];  // three whole load rounds
+
+    const int chunks = (p.max_context_len + kWgTokens - 1) / kWgTokens;
+    const int s = blockIdx.x / chunks;
+    const int n = idx_ctx(load_scalar(p.context_lens + s), p);
+    const int tok0 = (blockIdx.x - s * chunks) * kWgTokens;
+    if (tok0 >= n) return;  // the whole work-group
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g4 = lane >> 4;
-    const int wv = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int U = idx_total_units(p, lane);
-    const int per = (U + p.num_waves - 1) / p.num_waves;
-    const int g0 = wv * per;
-    const int g1 = min(U, g0 + per);
-    if (g0 >= g1) return;
 
-    const char* dummy = reinterpret_cast<const char*>(p.q);  // in-bounds source of loads past the range
-    IdxCursor cl = idx_locate(g0, p, lane);  // next unit to load
-    IdxCursor cc = cl;                        // next unit to score
+    // This wave's tokens and their block ids (lane u < 8 holds unit u's).
+    const int wtok0 = tok0 + wave * kWaveUnits * kIdxUnit;
+    const int nunits = min(kWaveUnits, max(0, (n - wtok0 + kIdxUnit - 1) / kIdxUnit));
+    int blk = -1;
+    if (lane < nunits) blk = p.block_tables[(int64_t)s * p.bt_stride + ((wtok0 + lane * kIdxUnit) >> p.block_size_log2)];
 
-    uint4 qop[HT][4];
-    float wt[HT];
-    int qseq = -1;
-    auto load_queries = [&](int s) __attribute__((always_inline)) {
-        const uint16_t* qs = p.q + ((size_t)s * p.num_heads + c) * 128;
+    // Queries and head weights, 16 bytes per thread per round; they go to LDS once the rows' loads
+    // are issued.
+    const char* qsrc = reinterpret_cast<const char*>(p.q + (size_t)s * p.num_heads * 128);
+    u32x4 qv[HT];
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                qop[ht][ks] = *reinterpret_cast<const uint4*>(qs + (size_t)ht * 16 * 128 + (ks >> 1) * 64 + 16 * g4 +
-                                                              8 * (ks & 1));
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) wt[ht] = p.w[(size_t)s * p.num_heads + 16 * ht + c];
-        // Wait here, inside the branch: where the branch rejoins the compiler would otherwise wait
-        // for every load in flight on every unit.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-        qseq = s;
-    };
+    for (int r = 0; r < HT; ++r) qv[r] = *reinterpret_cast<const u32x4*>(qsrc + (size_t)(r * 256 + tid) * 16);
+    const float wv = tid < HT * 16 ? p.w[(size_t)s * p.num_heads + tid] : 0.f;
 
-    // Block id of unit cl, read one unit ahead so that the scalar load's latency is hidden.
-    int pre_blk = 0;
-    auto fetch_block_id = [&]() __attribute__((always_inline)) {
-        if (cl.g < g1)
-            pre_blk = load_scalar(p.block_tables + (int64_t)cl.s * p.bt_stride + ((cl.k * kIdxUnit) >> p.block_size_log2));
-    };
-
-    // Loads unit cl (a unit past the range reads the queries instead) and advances cl.
-    auto load_unit = [&](RawUnit& r) __attribute__((always_inline)) {
-        const char* base = dummy;
-        const char* sbase = dummy;
-        r.ok = 0;
-        if (cl.g < g1) {
-            const int t0 = cl.k * kIdxUnit;
-            const int nv = min(kIdxUnit, cl.ctx - t0);
-            if ((uint32_t)pre_blk < (uint32_t)p.num_blocks) {
-                const char* unit = p.idx + (int64_t)pre_blk * p.block_stride + (int64_t)(t0 & (p.block_size - 1)) * kIdxRow;
-                base = unit + min(c, nv - 1) * kIdxRow;
-                sbase = unit + min(4 * g4 + (c & 3), nv - 1) * kIdxRow;
-                r.ok = 1;
-            }
+    // Issue every unit's flat loads: chunk r * 64 + lane of the unit's 2112 contiguous bytes (a unit
+    // never straddles a block). Units past the context or in an invalid block read the queries.
+    const char* dummy = qsrc;
+    u32x4 raw[kWaveUnits][3];  // a native vector type: a struct copy here would stay in scratch memory
+    bool unit_ok[kWaveUnits];
+#pragma unroll
+    for (int u = 0; u < kWaveUnits; ++u) {
+        const int b = __builtin_amdgcn_readlane(blk, u);
+        unit_ok[u] = u < nunits && (uint32_t)b < (uint32_t)p.num_blocks;
+        const char* base = unit_ok[u] ? p.idx + (int64_t)b * p.block_stride +
+                                            (int64_t)((wtok0 + u * kIdxUnit) & (p.block_size - 1)) * kIdxRow
+                                      : dummy;
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const int ch = min(r * 64 + lane, kUnitChunks - 1);
+            raw[u][r] = *reinterpret_cast<const u32x4*>(base + ch * 16);
         }
-        r.a = load16_a4(base + 16 * g4);
-        r.b = load16_a4(base + 64 + 16 * g4);
-        r.sc = *reinterpret_cast<const float*>(sbase + 128);
-        idx_advance(cl, p);
-        fetch_block_id();
-    };
+    }
 
-    auto score_unit = [&](const RawUnit& r) __attribute__((always_inline)) {
-        if (cc.s != qseq) load_queries(cc.s);
-        const int t0 = cc.k * kIdxUnit;
-        const int nv = min(kIdxUnit, cc.ctx - t0);
-        const uint4 kop[4] = {codes8_bf16(r.a.x, r.a.y), codes8_bf16(r.a.z, r.a.w), codes8_bf16(r.b.x, r.b.y),
-                              codes8_bf16(r.b.z, r.b.w)};
+#pragma unroll
+    for (int r = 0; r < HT; ++r) {
+        const int ch = r * 256 + tid;  // 16-byte chunk: head ch / 16, dims 8 (ch % 16) ..
+        *reinterpret_cast<u32x4*>(s_q + (ch >> 4) * kQRow + (ch & 15) * 16) = qv[r];
+    }
+    if (tid < HT * 16) s_w[tid] = wv;
+    __syncthreads();  // queries and weights in LDS
+    uint4 qop[HT][4];
+    float wr[HT][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qop[ht][ks] = *reinterpret_cast<const uint4*>(s_q + (16 * ht + c) * kQRow +
+                                                          ((ks >> 1) * 64 + 16 * g4 + 8 * (ks & 1)) * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wr[ht][j] = s_w[16 * ht + 4 * g4 + j];
+    }
+
+    // One basic block for all units (the scores are stored after the loop), so that the scheduler can
+    // overlap one unit's products with the next one's staging.
+    float score[kWaveUnits];
+#pragma unroll
+    for (int u = 0; u < kWaveUnits; ++u) {
+        // Stage the unit's bytes (two buffers, so that one unit's reads overlap the next one's
+        // writes), then read row c's key pieces and scale.
+        char* stage = s_stage[wave][u & 1];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) *reinterpret_cast<u32x4*>(stage + (r * 64 + lane) * 16) = raw[u][r];
+        const u32x4_a4 a = *reinterpret_cast<const u32x4_a4*>(stage + c * kIdxRow + 16 * g4);
+        const u32x4_a4 b = *reinterpret_cast<const u32x4_a4*>(stage + c * kIdxRow + 64 + 16 * g4);
+        const float sc = *reinterpret_cast<const float*>(stage + c * kIdxRow + 128);
+        const uint4 kop[4] = {codes8_bf16(a.x, a.y), codes8_bf16(a.z, a.w), codes8_bf16(b.x, b.y),
+                              codes8_bf16(b.z, b.w)};
         f32x4_t S[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) S[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) S[ht] = mfma_k32<true>(kop[ks], qop[ht][ks], S[ht]);
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int ht = 0; ht < HT; ++ht) S[ht] = mfma_k32<true>(qop[ht][ks], kop[ks], S[ht]);
+        float acc = 0.f;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = fmaf(wt[ht], fmaxf(S[ht][j], 0.f), acc[j]);
+            for (int j = 0; j < 4; ++j) acc = fmaf(wr[ht][j], fmaxf(S[ht][j], 0.f), acc);
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        score[u] = unit_ok[u] ? sc * acc : kNegInf;
+    }
+    if (g4 == 0) {
+        float* out = p.scores + (int64_t)s * p.score_stride + wtok0 + c;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = group_sum<16>(acc[j]);
-        const int jj = c & 3;
-        const float tot = jj == 0 ? acc[0] : jj == 1 ? acc[1] : jj == 2 ? acc[2] : acc[3];
-        const int t = 4 * g4 + jj;
-        if (c < 4 && t < nv) p.scores[(int64_t)cc.s * p.score_stride + t0 + t] = r.ok ? r.sc * tot : kNegInf;
-        idx_advance(cc, p);
-    };
-
-    fetch_block_id();
-    RawUnit r[kDepth];
-#pragma unroll
-    for (int i = 0; i < kDepth - 1; ++i) load_unit(r[i]);
-    bool more = true;
-    while (more) {
-#pragma unroll
-        for (int i = 0; i < kDepth; ++i) {
-            if (more) {
-                load_unit(r[(i + kDepth - 1) % kDepth]);
-                score_unit(r[i]);
-                more = cc.g < g1;
-            }
-        }
+        for (int u = 0; u < kWaveUnits; ++u)
+            if (u < nunits && wtok0 + u * kIdxUnit + c < n) out[u * kIdxUnit] = score[u];
     }
 }
 
@@ -249,7 +177,11 @@ namespace {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kTopkCache = 32768;  // scores of a sequence kept in LDS (128 KB); longer ones re-read
+constexpr int kTopkCache = 32768;  // scores of a sequence kept in LDS (128 KB); longer ones are re-read
+constexpr int kBtCache = 2048;     // block ids of a sequence kept in LDS
+constexpr int kPer = 8;            // consecutive positions per thread in the selection
+constexpr int kSelBlock = kPer * kTopkThreads;
+constexpr int kBins = 2048;        // 11-bit digits: bits 31..21, 20..10, then 9..0
 
 // Order-preserving key: a > b as floats <=> key(a) > key(b) as unsigned (-0 is taken as +0).
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -257,14 +189,30 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Work-group barrier for data in LDS: waits for this wave's LDS operations but not for its global
+// stores, which __syncthreads would also wait for.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    lds_barrier();
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl(v, max(lane - off, 0));
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(IndexerParams p) {
-    __shared__ float s_sc[kTopkCache];
-    __shared__ uint32_t s_hist[kTopkWaves][256];
-    __shared__ uint32_t s_tot[256];
+    __shared__ __attribute__((aligned(16))) float s_sc[kTopkCache];
+    __shared__ int32_t s_bt[kBtCache];
+    __shared__ uint32_t s_hist[2][kBins];
     __shared__ int s_pick[2];
-    __shared__ int s_wsum[2][kTopkWaves];
+    __shared__ int s_wsum[kTopkWaves][2];
 
     const int s = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -274,10 +222,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(IndexerParams p) {
     int32_t* slot_out = p.topk_slots + (int64_t)s * k;
     const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
     const float* src = p.scores + (int64_t)s * p.score_stride;
+    const int nblk = (n + p.block_size - 1) >> p.block_size_log2;
+    const bool bt_cached = nblk <= kBtCache;
 
     // Slot of position t (num_blocks * block_size fits in int32); -1 for an invalid block id.
-    auto slot_of = [&](int t) -> int32_t {
-        const int32_t b = bt[t >> p.block_size_log2];
+    auto slot_of = [&](int t) __attribute__((always_inline)) -> int32_t {
+        const int j = t >> p.block_size_log2;
+        const int32_t b = bt_cached ? s_bt[j] : bt[j];
         if ((uint32_t)b >= (uint32_t)p.num_blocks) return -1;
         return b * p.block_size + (t & (p.block_size - 1));
     };
@@ -285,111 +236,146 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(IndexerParams p) {
     if (tid == 0) p.topk_lens[s] = min(n, k);
     if (n <= k) {  // every token is selected
         for (int i = tid; i < k; i += kTopkThreads) {
+            int32_t sl = -1;
+            if (i < n) {
+                const int32_t b = bt[i >> p.block_size_log2];
+                sl = (uint32_t)b < (uint32_t)p.num_blocks ? b * p.block_size + (i & (p.block_size - 1)) : -1;
+            }
             pos_out[i] = i < n ? i : -1;
-            slot_out[i] = i < n ? slot_of(i) : -1;
+            slot_out[i] = sl;
         }
         return;
     }
 
+    // Scores (when they fit) and block ids -> LDS, kPer loads in flight per thread; zero histogram 0.
     const bool cached = n <= kTopkCache;
     if (cached) {
-        for (int i = tid; i < n; i += kTopkThreads) s_sc[i] = src[i];
-        __syncthreads();
+        for (int base = 0; base < n; base += kSelBlock) {
+            float v[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = base + j * kTopkThreads + tid;
+                v[j] = i < n ? src[i] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = base + j * kTopkThreads + tid;
+                if (i < n) s_sc[i] = v[j];
+            }
+        }
     }
-    auto key_at = [&](int i) __attribute__((always_inline)) { return order_key(cached ? s_sc[i] : src[i]); };
+    if (bt_cached)
+        for (int j = tid; j < nblk; j += kTopkThreads) s_bt[j] = bt[j];
+    for (int i = tid; i < kBins; i += kTopkThreads) s_hist[0][i] = 0u;
+    __syncthreads();
 
-    // Radix select: after the pass of digit d, `prefix` holds the top digits of the k-th largest key
-    // and `need` how many keys with that prefix still belong to the top k.
+    // Keys of positions base + kPer * tid + j (j < kPer); 0 past n.
+    auto keys_at = [&](int base, uint32_t (&key)[kPer]) __attribute__((always_inline)) {
+        const int i0 = base + kPer * tid;
+        if (cached && i0 + kPer <= n) {
+            const float4 a = *reinterpret_cast<const float4*>(s_sc + i0);
+            const float4 b = *reinterpret_cast<const float4*>(s_sc + i0 + 4);
+            key[0] = order_key(a.x);
+            key[1] = order_key(a.y);
+            key[2] = order_key(a.z);
+            key[3] = order_key(a.w);
+            key[4] = order_key(b.x);
+            key[5] = order_key(b.y);
+            key[6] = order_key(b.z);
+            key[7] = order_key(b.w);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = i0 + j;
+                key[j] = order_key(i < n ? (cached ? s_sc[i] : src[i]) : 0.f);
+            }
+        }
+    };
+
+    // Radix select: after each pass, `prefix` holds the top digits of the k-th largest key and
+    // `need` how many keys with that prefix still belong to the top k.
     uint32_t prefix = 0, mask = 0;
     int need = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&s_hist[0][0])[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < n; i += kTopkThreads) {
-            const uint32_t key = key_at(i);
-            if ((key & mask) == prefix) atomicAdd(&s_hist[wave][(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (tid < 256) {
-            uint32_t t = 0;
 #pragma unroll
-            for (int w = 0; w < kTopkWaves; ++w) t += s_hist[w][tid];
-            s_tot[tid] = t;
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // Lane l holds digits 255 - 4l - i (i = 0..3): the digits in descending order.
-            uint32_t cnt[4], sum = 0;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+        const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+        uint32_t* hist = s_hist[pass & 1];
+        for (int base = 0; base < n; base += kSelBlock) {
+            uint32_t key[kPer];
+            keys_at(base, key);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                cnt[i] = s_tot[255 - 4 * lane - i];
-                sum += cnt[i];
-            }
-            uint32_t incl = sum;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t t = __shfl(incl, max(lane - off, 0));
-                if (lane >= off) incl += t;
-            }
-            const uint32_t before = incl - sum;  // keys with a larger digit than this lane's first
-            if (before < (uint32_t)need && (uint32_t)need <= incl) {
-                uint32_t acc = before;
-                bool done = false;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (!done && acc + cnt[i] >= (uint32_t)need) {
-                        s_pick[0] = 255 - 4 * lane - i;
-                        s_pick[1] = (int)acc;
-                        done = true;
-                    }
-                    acc += cnt[i];
-                }
+            for (int j = 0; j < kPer; ++j) {
+                const int i = base + kPer * tid + j;
+                if (i < n && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
             }
         }
-        __syncthreads();
+        lds_sync();
+        // Thread t holds digits 2047 - 2t and 2046 - 2t (descending); a scan over them gives the keys
+        // above each digit, and the digit that holds the need-th key is picked. The other histogram
+        // is cleared for the next pass meanwhile.
+        const uint32_t c0 = hist[kBins - 1 - 2 * tid], c1 = hist[kBins - 2 - 2 * tid];
+        s_hist[(pass + 1) & 1][2 * tid] = 0u;
+        s_hist[(pass + 1) & 1][2 * tid + 1] = 0u;
+        int incl = wave_incl_scan((int)(c0 + c1), lane);
+        if (lane == 63) s_wsum[wave][0] = incl;
+        lds_sync();
+        for (int w = 0; w < wave; ++w) incl += s_wsum[w][0];
+        const uint32_t before = (uint32_t)incl - c0 - c1;  // keys above digit 2047 - 2t
+        if (before < (uint32_t)need && (uint32_t)need <= before + c0) {
+            s_pick[0] = kBins - 1 - 2 * tid;
+            s_pick[1] = (int)before;
+        } else if (before + c0 < (uint32_t)need && (uint32_t)need <= (uint32_t)incl) {
+            s_pick[0] = kBins - 2 - 2 * tid;
+            s_pick[1] = (int)(before + c0);
+        }
+        lds_sync();
         need -= s_pick[1];
         prefix |= (uint32_t)s_pick[0] << shift;
-        mask |= 255u << shift;
-        __syncthreads();
+        mask |= dmask << shift;
     }
 
     // Selection in position order: keys above the threshold, and the first `need` keys equal to it.
+    // A taken position i is output number gt_before(i) + min(eq_before(i), need).
     const uint32_t thr = prefix;
-    const uint64_t below = (1ull << lane) - 1ull;
-    int run_sel = 0, run_eq = 0;
-    for (int base = 0; base < n; base += kTopkThreads) {
-        const int i = base + tid;
-        const uint32_t key = i < n ? key_at(i) : 0u;
-        const bool gt = i < n && key > thr;
-        const bool eq = i < n && key == thr;
-        const uint64_t em = __builtin_amdgcn_ballot_w64(eq);
-        if (lane == 0) s_wsum[0][wave] = __builtin_popcountll(em);
-        __syncthreads();
-        int eq_rank = run_eq + __builtin_popcountll(em & below), eq_total = 0;
+    int run_gt = 0, run_eq = 0;
+    for (int base = 0; base < n; base += kSelBlock) {
+        uint32_t key[kPer];
+        keys_at(base, key);
+        int ngt = 0, neq = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const bool in = base + kPer * tid + j < n;
+            ngt += in && key[j] > thr;
+            neq += in && key[j] == thr;
+        }
+        const int packed = wave_incl_scan(ngt | (neq << 16), lane);  // both counts <= 512 per wave
+        if (lane == 63) s_wsum[wave][1] = packed;
+        lds_sync();
+        int before = packed - (ngt | (neq << 16)), total = 0;
 #pragma unroll
         for (int w = 0; w < kTopkWaves; ++w) {
-            const int v = s_wsum[0][w];
-            eq_rank += w < wave ? v : 0;
-            eq_total += v;
+            const int v = s_wsum[w][1];
+            before += w < wave ? v : 0;
+            total += v;
         }
-        const bool take = gt || (eq && eq_rank < need);
-        const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
-        if (lane == 0) s_wsum[1][wave] = __builtin_popcountll(tm);
-        __syncthreads();
-        int out = run_sel + __builtin_popcountll(tm & below), sel_total = 0;
+        int gt_before = run_gt + (before & 0xFFFF), eq_before = run_eq + (before >> 16);
+        run_gt += total & 0xFFFF;
+        run_eq += total >> 16;
 #pragma unroll
-        for (int w = 0; w < kTopkWaves; ++w) {
-            const int v = s_wsum[1][w];
-            out += w < wave ? v : 0;
-            sel_total += v;
+        for (int j = 0; j < kPer; ++j) {
+            const int i = base + kPer * tid + j;
+            const bool in = i < n;
+            const bool gt = in && key[j] > thr, eq = in && key[j] == thr;
+            const int out = gt_before + min(eq_before, need);
+            if ((gt || (eq && eq_before < need)) && out < k) {  // exactly k are taken; the bound is a guard
+                pos_out[out] = i;
+                slot_out[out] = slot_of(i);
+            }
+            gt_before += gt;
+            eq_before += eq;
         }
-        if (take && out < k) {  // exactly k are taken; the bound keeps a broken invariant in bounds
-            pos_out[out] = i;
-            slot_out[out] = slot_of(i);
-        }
-        run_sel += sel_total;
-        run_eq += eq_total;
-        __syncthreads();
+        lds_sync();
     }
 }
 
@@ -397,7 +383,8 @@ namespace {
 
 template <int HT>
 hipError_t launch_scores(const IndexerParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((indexer_score_kernel<HT>), dim3((unsigned)(p.num_waves / 4)), dim3(256), 0, stream, p);
+    const int64_t wgs = (int64_t)((p.max_context_len + kWgTokens - 1) / kWgTokens) * p.num_seqs;
+    hipLaunchKernelGGL((indexer_score_kernel<HT>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -405,13 +392,15 @@ hipError_t launch_scores(const IndexerParams& p, hipStream_t stream) {
 
 hipError_t launch_indexer_topk(const IndexerParams& p, hipStream_t stream) {
     if (p.num_seqs <= 0) return hipSuccess;
-    hipError_t e;
-    switch (p.num_heads) {
-        case 16: e = launch_scores<1>(p, stream); break;
-        case 32: e = launch_scores<2>(p, stream); break;
-        case 48: e = launch_scores<3>(p, stream); break;
-        case 64: e = launch_scores<4>(p, stream); break;
-        default: return hipErrorInvalidValue;
+    hipError_t e = hipSuccess;
+    if (p.max_context_len > 0) {
+        switch (p.num_heads) {
+            case 16: e = launch_scores<1>(p, stream); break;
+            case 32: e = launch_scores<2>(p, stream); break;
+            case 48: e = launch_scores<3>(p, stream); break;
+            case 64: e = launch_scores<4>(p, stream); break;
+            default: return hipErrorInvalidValue;
+        }
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_kernel, dim3((unsigned)p.num_seqs), dim3(kTopkThreads), 0, stream, p);

@@ -172,7 +172,6 @@ struct IndexerParams {
     int32_t block_size;
     int32_t block_size_log2;
     int32_t max_context_len;   // clamp for context_lens
-    int32_t num_waves;         // waves of the score kernel's grid
     int32_t top_k;
 };
 hipError_t launch_indexer_topk(const IndexerParams& p, hipStream_t stream);

@@ -470,6 +470,7 @@ def run_dsa_sparse(case, img, idx_v, descs, tables, lens, steps, warmup):
         "sparse_decode_tflops": tf,
         "sparse_decode_mfma_frac": tf / MFMA_BF16_PEAK_TF,
         "sparse_decode_gbs": dec_bytes / (dec_ms / 1e3) / 1e9,
+        "sparse_decode_traffic": traffic_for("dsa_sparse"),
         "selected_tokens": int(sel.sum()),
     }
 

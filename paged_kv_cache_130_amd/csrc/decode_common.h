@@ -159,25 +159,48 @@ __device__ __forceinline__ bool find_work(int w, const DenseDecodeParams& p, int
 template <bool BF16, int D>
 __device__ __forceinline__ void merge_partials(const float* ml, int64_t ml_stride, const float* acc,
                                                int64_t acc_stride, int n, uint16_t* out) {
-    constexpr int DPL = D / 64;  // output values per lane
-    constexpr int U = 16;        // partials per unrolled step
+    constexpr int DPL = D / 64;            // output values per lane
+    constexpr int U = 16;                  // partials per unrolled step
+    constexpr int P = D >= 512 ? 8 : 16;   // partials loaded before their weights are known
     const int lane = threadIdx.x & 63;
-    float M = kNegInf;
-    for (int i = lane; i < n; i += 64) M = fmaxf(M, ml[i * ml_stride]);
+    const float* ap = acc + lane * DPL;
+    // The first P partials' accumulators go out with the (m, l) loads, so that the common case (at
+    // most P partials) waits for memory once. Indexes past n - 1 load the last partial again; their
+    // weight is 0.
+    float v0[P][DPL];
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+        const int jj = min(u, n - 1);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) v0[u][k] = ap[jj * acc_stride + k];
+    }
+    float mi = kNegInf, li = 0.f;
+    if (lane < n) {
+        mi = ml[lane * ml_stride];
+        li = ml[lane * ml_stride + 1];
+    }
+    float M = mi;
+    for (int i = lane + 64; i < n; i += 64) M = fmaxf(M, ml[i * ml_stride]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float L = 0.f;
-    for (int i = lane; i < n; i += 64) L += fast_exp2(ml[i * ml_stride] - M) * ml[i * ml_stride + 1];
+    float L = lane < n ? fast_exp2(mi - M) * li : 0.f;
+    for (int i = lane + 64; i < n; i += 64) L += fast_exp2(ml[i * ml_stride] - M) * ml[i * ml_stride + 1];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
     const float invL = L > 0.f ? 1.f / L : 0.f;
+    const float w0 = lane < n ? fast_exp2(mi - M) * invL : 0.f;  // partial `lane`'s weight
     float a[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) a[k] = 0.f;
-    const float* ap = acc + lane * DPL;
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), u));
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) a[k] = fmaf(w, v0[u][k], a[k]);
+    }
     for (int base = 0; base < n; base += 64) {
         const int i = base + lane;
-        const float wl = i < n ? fast_exp2(ml[i * ml_stride] - M) * invL : 0.f;  // 0 past the last partial
+        const float wl = base == 0 ? w0 : (i < n ? fast_exp2(ml[i * ml_stride] - M) * invL : 0.f);
         const int cnt = min(64, n - base);
         // Full steps of U partials, then steps of 4; indexes past cnt - 1 load a valid duplicate
         // whose weight is 0.
@@ -197,7 +220,7 @@ __device__ __forceinline__ void merge_partials(const float* ml, int64_t ml_strid
                 for (int k = 0; k < DPL; ++k) a[k] = fmaf(w, v[u][k], a[k]);
             }
         };
-        int j0 = 0;
+        int j0 = base == 0 ? P : 0;  // the first P partials are already in
         for (; j0 + U <= cnt; j0 += U) step(std::integral_constant<int, U>{}, j0);
         for (; j0 < cnt; j0 += 4) step(std::integral_constant<int, 4>{}, j0);
     }

@@ -182,9 +182,10 @@ __device__ __forceinline__ uint4 dequant8(uint2 b, float sc) {
 
 }  // namespace
 
-// NW: waves per work-group; each wave owns 16 heads (heads_per_wg = 16 * NW). With 8 waves (128
-// heads) two waves share each SIMD, so one wave's vector and LDS work overlaps the other's MFMAs;
-// that caps a wave at 256 registers: 128 accumulators for its 16 x 512 output, 72 for its queries.
+// NW: waves per work-group (4, 2 or 1); each wave owns 16 heads (heads_per_wg = 16 * NW). A wave
+// holds 128 accumulators for its 16 x 512 output and 72 registers of queries, about 420 registers
+// in all, so one wave runs per SIMD. (Eight waves, two per SIMD, would each have to fit in 256
+// registers; compiled that way the kernel spills.)
 //
 // SPARSE: token i of sequence s is the row at slot slots[s][i], in any block. The slots of a unit are
 // copied into LDS (s_slot) along with the rows of the unit four places earlier, so each lane finds

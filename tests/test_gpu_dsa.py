@@ -262,3 +262,23 @@ def test_full_size_dsa_sparse_sampled():
         view = P.CacheView(0, 0, bs * 656, 656)
         want = D.sparse_mla_decode(q[b:b + 1], image, view, 0, [pos[b, :lens[b]]], bs, nb, case.scale)
         assert_close(got[b], want[0], MLA_ATOL, MLA_RTOL, f"seq {b} (ctx {n})")
+
+
+def test_many_sequences_and_uncached_block_ids():
+    # 300 sequences (five 64-sequence passes of the sparse decode's unit search) with short and empty contexts,
+    # and one 40,000-token sequence at block size 16, whose 2500 block ids exceed the selection
+    # kernel's LDS copy (slots are then looked up in memory).
+    rng = np.random.default_rng(21)
+    ctx = rng.integers(0, 90, size=300).tolist()
+    case, img, host = dsa_case(4500, ctx, 16, 16, 16)
+    mla_v, _, _ = views(16)
+    res = run_topk(case, img, 1, 24)
+    check_topk(case, host, 1, 24, res)
+    _, _, slots, lens = res
+    got = sparse_decode(case, img, 1, slots, lens, 24)
+    want = D.sparse_mla_decode(bits_np(case.q), host, mla_v, 1, [slots[b, :lens[b]] for b in range(len(ctx))], 16,
+                               case.num_blocks, case.scale)
+    assert_close(got, want, MLA_ATOL, MLA_RTOL, "300 sequences")
+    long_case, long_img, long_host = dsa_case(4600, [40000], 16, 16, 16)
+    res = run_topk(long_case, long_img, 0, 1000)
+    check_topk(long_case, long_host, 0, 1000, res)

@@ -33,7 +33,8 @@ FP8_SCALE = 2.0 ** -5       # K and V scale of the FP8 cache variants (N(0,1) va
 MFMA_BF16_PEAK_TF = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = ("api.hip", "cache_write.hip", "decode_dense.hip", "decode_fp8.hip", "decode_mfma.hip", "decode_mla.hip",
-                  "dsa_indexer.hip", "prefill_mfma.hip", "decode_common.h", "decode_mfma.h", "mfma_common.h", "pa_device.h", "pa_internal.h")
+                  "dsa_indexer.hip", "prefill_mfma.hip", "decode_common.h", "decode_mfma.h",
+                  "decode_mla.h", "mfma_common.h", "pa_device.h", "pa_internal.h")
 
 
 def kernel_source_hash() -> str:

@@ -21,6 +21,9 @@ LIB = os.path.join(PKG, "libpa.so")
 
 SOURCES = ["api.hip", "cache_write.hip", "decode_dense.hip", "decode_fp8.hip", "decode_mfma.hip", "prefill_mfma.hip",
            "decode_mla.hip", "dsa_indexer.hip"]
+# Per-source flags. The MLA decode keeps its MFMA accumulators in ordinary vector registers, so that
+# two of its waves fit per SIMD (see decode_mla.hip).
+EXTRA_FLAGS = {"decode_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -46,7 +49,7 @@ def build(verbose: bool = False) -> str:
     objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
 
     def compile_one(i):
-        return _run([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]])
+        return _run([HIPCC, *CFLAGS, *EXTRA_FLAGS.get(SOURCES[i], []), "-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]])
 
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         logs = list(ex.map(compile_one, range(len(SOURCES))))

@@ -44,6 +44,30 @@ __device__ __forceinline__ void lds_barrier() {
     compiler_fence();
 }
 
+// Byte address in LDS of p, a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct-to-LDS copy of BYTES (4 or 16) per lane: lane i's BYTES at src land at LDS byte address
+// lds + BYTES * i (lds is wave-uniform). It is the instruction __builtin_amdgcn_global_load_lds
+// emits, issued through inline asm. The compiler counts the builtin as an outstanding flat access to
+// LDS, and while one is in flight it waits for any LDS read by draining all LDS operations
+// (lgkmcnt(0)), which in a pipeline that always has copies in flight defeats every operand prefetch.
+// Hidden from the compiler, the copy is ordered only by the caller: an s_waitcnt vmcnt for its own
+// copies, then a barrier, before anything reads the destination, and an s_waitcnt vmcnt(0) before
+// the kernel ends. M0 (which the instruction takes the LDS address from) is set inside the asm; the
+// kernels that use this helper use M0 for nothing else.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* src, uint32_t lds) {
+    static_assert(BYTES == 4 || BYTES == 16, "4 or 16 bytes per lane");
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory");
+}
+
 // v_perm_b32 selectors: low 16-bit halves of (a, b) -> (a.lo, b.lo); high halves -> (a.hi, b.hi).
 constexpr uint32_t kSelLo = 0x05040100u;
 constexpr uint32_t kSelHi = 0x07060302u;

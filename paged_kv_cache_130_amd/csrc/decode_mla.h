@@ -1,0 +1,665 @@
+// MLA latent decode over packed 656-byte rows: many query heads on one latent K/V head.
+//
+// "deep dive into vLLM 05" §3.3: MLA caches one low-dimensional latent per token; with the
+// up-projection folded into the query, attention runs in latent space and the cache is never
+// decompressed. "vLLM KV Cache Layout 可视化" (section on two caches sharing one block table) gives
+// the row: 512 B of FP8 latent, 16 B of scale, 128 B of BF16 RoPE. The row is read here as 512 e4m3
+// latent values, 4 float32 scales (scale k for latent values [128k, 128k+128)) and 64 bf16 RoPE
+// values. Scores use [latent | rope] (576 dims); the value is the dequantized 512-dim latent:
+//     s_t = scale * (q_lat . (c_t * sc_t) + q_rope . r_t),   out = softmax(s) . (c * sc).
+//
+// With 128 heads on one latent head the work is a dense contraction: per token 128 x (576 + 512)
+// multiply-adds against 656 bytes read, about 425 flop per byte, above the MI355X bf16 ridge
+// (2.5 PFLOP/s over 8 TB/s, about 310). So the kernel is laid out for the matrix cores:
+//
+//  * A work-group owns up to 64 heads (128 heads take two head groups) and a balanced range of the
+//    token stream (all sequences' 32-token units, in order; ranges may cross sequences). Each of its
+//    waves owns 16 heads and one half (256 dims) of their outputs: two waves per 16 heads, up to
+//    eight waves, two per SIMD. A wave holds its heads' queries (18 k-steps, 72 registers) and its
+//    outputs (16 heads x 256 fp32, 64 registers) for a whole segment, so the only operands streamed
+//    are K and V. The two waves of a head group both compute the group's scores and softmax (the
+//    same values), which costs a third more products than splitting them but needs no exchange;
+//    with a second wave per SIMD one wave's softmax and dequantization run beside the other's
+//    products. (One wave per 16 heads and all 512 output dims needs about 420 registers, so only
+//    one wave fits per SIMD.)
+//  * Each 32-token unit is copied from HBM straight into LDS (lds_dma, 16 bytes per lane, four
+//    stages in flight), then dequantized once per work-group into a bf16 tile
+//    [32 rows x (512 latent * scale | 64 RoPE)]: each e4m3 value is converted exactly to fp32,
+//    multiplied by its scale and rounded to bf16. Every wave reads its score (K) and PV (V) operands
+//    from that tile; rows are swizzled so the operand reads are free of bank conflicts.
+//  * Scores S^T = K . Q^T and PV O += P . V run on v_mfma_f32_16x16x32_bf16. The score output
+//    registers are directly the PV A operand (token order sigma of mfma_common.h, two 16-token tiles
+//    per k=32 step); the V operand comes from ds_read_b64_tr_b16, which transposes 4 x 4 blocks of
+//    16-bit values across the lanes of a 16-lane group.
+//  * Per unit: one barrier; the dequantization of unit u+1 is interleaved with the products of
+//    unit u, and operands are loaded four products ahead. The softmax is online (lazy reference, as
+//    in the dense decode) and a segment that is not a whole sequence writes an fp32 partial merged
+//    by mla_merge_kernel (log-sum-exp).
+
+#pragma once
+
+#include "decode_common.h"
+#include "mfma_common.h"
+
+namespace pa {
+
+namespace {
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRow = 656;                          // bytes per cached token row
+constexpr int kScaleOff = 512;                     // 4 x float32
+constexpr int kRopeOff = 528;                      // 64 x bf16
+constexpr int kUnit = 32;                          // tokens per unit (one step of a work-group)
+constexpr int kUnitChunks = kUnit * kRow / 16;     // 1312 chunks of 16 bytes; 41 per row
+constexpr int kWindows = (kUnitChunks + 63) / 64;  // one load instruction of a wave fills a 64-chunk window
+constexpr int kRawStage = kWindows * 1024;
+constexpr int kTileRow = 1152;                     // 576 bf16
+constexpr int kTileStage = kUnit * kTileRow;
+constexpr int kTile1 = 16 * kTileRow;              // byte offset of the unit's second 16-token tile
+constexpr int kLatentChunks = kUnit * 64;          // 16-byte bf16 chunks of dequantized latent per unit
+constexpr int kRopeChunks = kUnit * 8;
+constexpr int kKSteps = 18;                        // k=32 steps over 576 score dims
+
+// Raw rows arrive in four stages and the dequantized tile has two. They are separate objects rather
+// than one indexed array so that the compiler can tell the stage being read from those still being
+// filled by the direct-to-LDS loads, and does not wait for all of them.
+__shared__ __attribute__((aligned(16))) char s_raw0[kRawStage];
+__shared__ __attribute__((aligned(16))) char s_raw1[kRawStage];
+__shared__ __attribute__((aligned(16))) char s_raw2[kRawStage];
+__shared__ __attribute__((aligned(16))) char s_raw3[kRawStage];
+__shared__ __attribute__((aligned(16))) char s_junk[1024];  // target of loads past the last window
+__shared__ __attribute__((aligned(16))) char s_tile0[kTileStage];
+__shared__ __attribute__((aligned(16))) char s_tile1[kTileStage];
+// Sparse form: the slots of unit g (32 used of 64 entries) in table g % 8, copied four units ahead.
+__shared__ __attribute__((aligned(16))) int32_t s_slot[8][64];
+
+template <int K>
+__device__ __forceinline__ char* raw_stage() {
+    if constexpr (K == 0) return s_raw0;
+    else if constexpr (K == 1) return s_raw1;
+    else if constexpr (K == 2) return s_raw2;
+    else return s_raw3;
+}
+template <int K>
+__device__ __forceinline__ char* tile_stage() {
+    if constexpr (K == 0) return s_tile0;
+    else return s_tile1;
+}
+
+// 16-byte chunk c of tile row r is stored at chunk c ^ swz(r). Tile rows are 1152 bytes, a multiple
+// of the 128-byte bank cycle, so unswizzled the rows read together would collide. With this swizzle
+// the eight rows a group of eight lanes reads for the score operand (16t + sigma(m), m = 0..7 or
+// 8..15) get eight different swizzles, and the rows g4 + 4i read for the value operand differ in
+// the swizzle's upper two bits.
+__device__ __forceinline__ int swz(int r) { return (((r >> 2) & 3) << 1) | (r & 1); }
+
+__device__ __forceinline__ int clamp_ctx(int64_t ctx, const MlaDecodeParams& p) {
+    const int64_t row = p.slots != nullptr ? p.slot_stride : (int64_t)p.bt_stride * p.block_size;
+    const int64_t cap = min((int64_t)p.max_context_len, row);
+    return (int)max((int64_t)0, min(ctx, cap));
+}
+
+// Context of sequence s (per lane).
+__device__ __forceinline__ int mla_ctx(int s, const MlaDecodeParams& p) { return clamp_ctx(p.context_lens[s], p); }
+
+// Context of sequence s, s wave-uniform.
+__device__ __forceinline__ int mla_ctx_uniform(int s, const MlaDecodeParams& p) {
+    return clamp_ctx(load_scalar(p.context_lens + s), p);
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// Position in the unit stream (all values wave-uniform).
+struct Cursor {
+    int g;    // unit index in the whole stream
+    int s;    // sequence
+    int k;    // unit within the sequence
+    int nu;   // units of the sequence
+    int ctx;  // tokens of the sequence
+};
+
+__device__ __forceinline__ void advance(Cursor& c, const MlaDecodeParams& p) {
+    ++c.g;
+    if (++c.k < c.nu) return;
+    c.k = 0;
+    do {
+        ++c.s;
+        c.ctx = c.s < p.num_seqs ? mla_ctx_uniform(c.s, p) : 0;
+        c.nu = (c.ctx + kUnit - 1) / kUnit;
+    } while (c.nu == 0 && c.s < p.num_seqs);
+}
+
+__device__ int total_units(const MlaDecodeParams& p, int lane) {
+    int u = 0;
+    for (int base = 0; base < p.num_seqs; base += 64) {
+        const int s = base + lane;
+        u += wave_sum_int(s < p.num_seqs ? (mla_ctx(s, p) + kUnit - 1) / kUnit : 0);
+    }
+    return __builtin_amdgcn_readfirstlane(u);
+}
+
+// Cursor of unit g0 (g0 < total_units).
+__device__ Cursor locate(int g0, const MlaDecodeParams& p, int lane) {
+    int before = 0;
+    for (int base = 0; base < p.num_seqs; base += 64) {
+        const int s = base + lane;
+        const int ctx = s < p.num_seqs ? mla_ctx(s, p) : 0;
+        const int nu = (ctx + kUnit - 1) / kUnit;
+        int incl = nu;  // inclusive prefix over the lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl(incl, max(lane - off, 0));
+            if (lane >= off) incl += t;
+        }
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (g0 < before + total) {
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(before + incl > g0);
+            const int ls = __builtin_ctzll(hit);
+            Cursor c;
+            c.g = g0;
+            c.s = base + ls;
+            c.ctx = __builtin_amdgcn_readlane(ctx, ls);
+            c.nu = __builtin_amdgcn_readlane(nu, ls);
+            c.k = g0 - (before + __builtin_amdgcn_readlane(incl, ls) - c.nu);
+            return c;
+        }
+        before += total;
+    }
+    Cursor c{g0, p.num_seqs, 0, 0, 0};
+    return c;
+}
+
+// Eight e4m3 bytes, times their row-quarter scale, as eight bf16 (round to nearest even). The
+// e4m3 -> fp32 conversion is exact.
+__device__ __forceinline__ uint4 dequant8(uint2 b, float sc) {
+    const f32x2_t a0 = __builtin_amdgcn_cvt_pk_f32_fp8(b.x, false);
+    const f32x2_t a1 = __builtin_amdgcn_cvt_pk_f32_fp8(b.x, true);
+    const f32x2_t a2 = __builtin_amdgcn_cvt_pk_f32_fp8(b.y, false);
+    const f32x2_t a3 = __builtin_amdgcn_cvt_pk_f32_fp8(b.y, true);
+    return make_uint4(pack2<true>(a0.x * sc, a0.y * sc), pack2<true>(a1.x * sc, a1.y * sc),
+                      pack2<true>(a2.x * sc, a2.y * sc), pack2<true>(a3.x * sc, a3.y * sc));
+}
+
+}  // namespace
+
+// NW: waves per work-group (8, 4 or 2); waves w and w + NW / 2 own the same 16 heads
+// (heads_per_wg = 8 * NW) and output dims [0, 256) and [256, 512). A wave needs about 235
+// registers, which fit the 256 that two waves per SIMD leave each only when the MFMA accumulators
+// are ordinary vector registers: decode_mla.hip is compiled with -mllvm -amdgpu-mfma-vgpr-form.
+//
+// SPARSE: token i of sequence s is the row at slot slots[s][i], in any block. The slots of a unit are
+// copied into LDS (s_slot) along with the rows of the unit four places earlier, so each lane finds
+// the row of each of its 16-byte chunks there when it issues the unit's copy; a row whose slot is
+// outside the pool, or past the sequence's count, is read from q and masked out.
+template <int NW, bool SPARSE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4 > 1 ? 2 : 1, 2)))
+void decode_mla_kernel(MlaDecodeParams p) {
+    constexpr int R = (kWindows + NW - 1) / NW;  // row-copy instructions per lane per unit
+    constexpr int RL = R + (SPARSE ? 1 : 0);     // all copy instructions per lane per unit
+    constexpr int kLatentIters = kUnit / NW;     // tile rows each wave dequantizes per unit
+    constexpr int kRopeIters = (kRopeChunks + 64 * NW - 1) / (64 * NW);
+    static_assert(NW == 2 || NW == 4 || NW == 8, "two to eight waves");
+    constexpr int kHeadWaves = NW / 2;
+    constexpr int kDimTiles = 16;                // 16-dim output tiles of this wave (256 dims)
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int lane = threadIdx.x & 63;
+    int tid = wave * 64 + lane;
+    const int w = blockIdx.x;
+    const int Hq = p.num_q_heads;
+    const int hwave = wave % kHeadWaves;
+    const int half = wave / kHeadWaves;  // output dims [256 half, +256)
+    const int head0 = blockIdx.y * p.heads_per_wg + hwave * 16;  // first head of this wave
+
+    const int U = total_units(p, lane);
+    const int per = p.units_per_wg > 0 ? p.units_per_wg : (U + p.num_wgs - 1) / p.num_wgs;
+    const int g_begin = w * per;
+    const int g_end = min(U, g_begin + per);
+    if (g_begin >= g_end) return;  // the same for every wave of the work-group
+
+    const char* dummy = static_cast<const char*>(p.q);  // in-bounds source of loads that fill nothing used
+    const uint32_t nb = (uint32_t)p.num_blocks;
+    const float sl2 = p.scale_log2;
+
+    // Per-lane LDS offsets (c = lane % 16, g4 = lane / 16).
+    // Score operand (A = K): row 16t + sigma(c), chunk 4ks + g4, swizzled: the physical chunk is
+    // 8 (ks >> 1) + ((4 (ks & 1)) ^ x) with x = g4 ^ swz(row).
+    int a_even, a_odd;
+    // Value operand (B = V), read with ds_read_b64_tr_b16: in each 16-lane block (lane group g4) lane
+    // n supplies the address of 4 dims (16dt + 4 (n & 3) .. +3) of row 16t + g4 + 4 (n >> 2), and lane
+    // i receives dim 16dt + i of the four rows g4, g4 + 4, g4 + 8, g4 + 12: exactly k-slots 0..3
+    // (t = 0) or 4..7 (t = 1) of a 16x16x32 B operand whose column i is dim 16dt + i. The physical
+    // chunk of that 8-byte piece is 8 (dt >> 2) + 2 ((dt & 3) ^ j) + (h ^ (g4 & 1)) with j = n >> 2,
+    // h = (n >> 1) & 1; trbase[d3] holds everything but the dt >> 2 part, for d3 = dt & 3.
+    int trbase[4];
+    auto lane_offsets = [&]() __attribute__((always_inline)) {
+        const int c = lane & 15, g4 = lane >> 4;
+        const int arow = sigma(c);
+        const int ax = g4 ^ swz(arow);
+        a_even = arow * kTileRow + (ax << 4);
+        a_odd = arow * kTileRow + ((ax ^ 4) << 4);
+        const int j = c >> 2, h = (c >> 1) & 1;
+#pragma unroll
+        for (int d3 = 0; d3 < 4; ++d3)
+            trbase[d3] = (g4 + 4 * j) * kTileRow + ((2 * (d3 ^ j) + (h ^ (g4 & 1))) << 4) + ((c & 1) << 3);
+    };
+    lane_offsets();
+
+    uint4 qr[kKSteps];
+    f32x4_t O[kDimTiles];  // register j of lane (c, g4): head 4 g4 + j, dim 16 (dt0 + dt) + c
+    const int dt0 = half * kDimTiles;
+    float m = kNegInf, l = 0.f;
+    // Unit validity, one mask per raw stage: bit r set when row r holds a token of the unit.
+    uint32_t info[4];
+
+    Cursor cc = locate(g_begin, p, lane);  // unit being computed
+    Cursor cl = cc;                        // next unit to load
+    Cursor cs = cc;                        // sparse: next unit whose slot table is copied
+    bool seg_from_start = false;           // the current segment began at the sequence's first unit
+
+    // Row copy. Chunk kk of a unit (41 per row) is loaded by lane kk % 64 of wave (kk / 64) % NW in
+    // round kk / (64 NW). A lane whose chunk is past the unit's valid rows reloads the last valid
+    // chunk into its own LDS slot (a row that is never read); a unit with no valid rows (past the
+    // range, or in an invalid block) reads the first 16 bytes of q instead. So every wave issues the
+    // same R loads per unit, which the vmcnt accounting relies on.
+    int dma_kk[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) dma_kk[r] = (r * NW + wave) * 64 + lane;
+
+    // Block ids of unit cl (pre_pb: rows 16..31 when block_size is 16). A step reads them before its
+    // opening wait, which also waits for them, so that their latency is hidden by that wait and no
+    // scalar load is outstanding during the products: scalar loads return out of order, so while
+    // one is pending every wait for LDS data would have to wait for all of it.
+    int pre_pa = 0, pre_pb = 0;
+    auto prefetch_ids = [&]() __attribute__((always_inline)) {
+        if (!SPARSE && cl.g < g_end) {
+            const int t0 = cl.k * kUnit;
+            const int32_t* bt = p.block_tables + (int64_t)cl.s * p.bt_stride;
+            const int lb = t0 >> p.block_size_log2;
+            pre_pa = load_scalar(bt + lb);
+            pre_pb = (p.block_size < kUnit && cl.ctx - t0 > 16) ? load_scalar(bt + lb + 1) : pre_pa;
+        }
+    };
+
+    // Copies unit cl into raw stage K, records its validity in info[K] and advances cl.
+    // Slot table of unit cs: wave 0 copies 64 entries (the unit's 32, then the next 32, clamped to the
+    // sequence) into s_slot[cs.g % 8]; the other waves issue the same instruction into s_junk, so that
+    // every wave counts RL copies per unit.
+    auto copy_slot_table = [&]() __attribute__((always_inline)) {
+        const int32_t* src = p.slots;
+        if (cs.g < g_end) src = p.slots + (int64_t)cs.s * p.slot_stride + min(cs.k * kUnit + lane, cs.ctx - 1);
+        lds_dma<4>(src, wave == 0 ? lds_addr(s_slot[0]) + 256 * (cs.g & 7) : lds_addr(s_junk));
+        advance(cs, p);
+    };
+
+    auto issue_sparse = [&](auto kst) __attribute__((always_inline)) {
+        constexpr int K = decltype(kst)::value;
+        const int v = cl.g < g_end ? min(kUnit, cl.ctx - cl.k * kUnit) : 0;
+        const int32_t* tab = s_slot[cl.g & 7];
+        const uint32_t nslots = (uint32_t)p.num_slots;
+        const int32_t mine = tab[lane & 31];
+        info[K] = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && lane < v && (uint32_t)mine < nslots);
+        char* stage = raw_stage<K>();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int win = r * NW + wave;
+            const int kk = dma_kk[r];
+            const int row = kk / 41;  // >= 32 past the unit's last chunk
+            const int32_t sl = tab[row & 31];
+            const bool ok = row < v && (uint32_t)sl < nslots;
+            const char* src = ok ? p.kv + (int64_t)(sl >> p.block_size_log2) * p.block_stride +
+                                       (int64_t)(sl & (p.block_size - 1)) * kRow + (kk - row * 41) * 16
+                                 : dummy;
+            lds_dma<16>(src, win < kWindows ? lds_addr(stage) + win * 1024 : lds_addr(s_junk));
+        }
+        copy_slot_table();
+        advance(cl, p);
+    };
+
+    auto issue = [&](auto kst) __attribute__((always_inline)) {
+        constexpr int K = decltype(kst)::value;
+        if constexpr (SPARSE) {
+            issue_sparse(kst);
+            return;
+        }
+        const bool live = cl.g < g_end;
+        int v = 0;
+        const char* base_a = dummy;              // rows 0..15 (all rows when block_size >= 32)
+        const char* base_b = dummy - 16 * kRow;  // rows 16..31, addressed by chunk kk >= 16 * 41
+        int lim_a = 0, lim_b = 16 * 41;
+        bool ok_a = false, ok_b = false;
+        if (live) {
+            v = min(kUnit, cl.ctx - cl.k * kUnit);
+            const int t0 = cl.k * kUnit;
+            const int pa = pre_pa;
+            ok_a = (uint32_t)pa < nb;
+            if (p.block_size >= kUnit) {
+                ok_b = ok_a;
+                if (ok_a) {
+                    base_a = p.kv + (int64_t)pa * p.block_stride + (int64_t)(t0 & (p.block_size - 1)) * kRow;
+                    lim_a = v * 41 - 1;
+                }
+            } else {  // block size 16: rows 16..31 are in the next block
+                if (ok_a) {
+                    base_a = p.kv + (int64_t)pa * p.block_stride;
+                    lim_a = min(v, 16) * 41 - 1;
+                }
+                if (v > 16) {
+                    const int pb = pre_pb;
+                    ok_b = (uint32_t)pb < nb;
+                    if (ok_b) {
+                        base_b = p.kv + (int64_t)pb * p.block_stride - 16 * kRow;
+                        lim_b = v * 41 - 1;
+                    }
+                }
+            }
+        }
+        info[K] = (v >= 32 ? 0xFFFFFFFFu : (1u << v) - 1u) & ((ok_a ? 0xFFFFu : 0u) | (ok_b ? 0xFFFF0000u : 0u));
+        char* stage = raw_stage<K>();
+        const bool split = p.block_size < kUnit;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int win = r * NW + wave;
+            const int kk = dma_kk[r];
+            const bool hi = split && kk >= 16 * 41;
+            const char* src = (hi ? base_b : base_a) + (int64_t)min(kk, hi ? lim_b : lim_a) * 16;
+            lds_dma<16>(src, win < kWindows ? lds_addr(stage) + win * 1024 : lds_addr(s_junk));
+        }
+        advance(cl, p);
+    };
+
+    // Dequantization of a unit: raw stage KR (validity vi) -> tile stage KT. Item it is row
+    // it * NW + wave (the same for the whole wave), 8 bytes per lane; rows past the valid ones write
+    // zeros (their stale LDS bytes are read but not used). conv_load issues the LDS reads of all
+    // items; conv_store converts and writes items [i0, i0 + CNT) and, if rope, the RoPE chunks.
+    struct ConvIn {
+        uint2 b8[kLatentIters];
+        float sc[kLatentIters];
+    };
+    auto conv_load = [&](auto kr, ConvIn& in) __attribute__((always_inline)) {
+        constexpr int KR = decltype(kr)::value;
+        const char* raw = raw_stage<KR>();
+        const int conv_raw = wave * kRow + 8 * lane;
+        const int conv_scale = wave * kRow + kScaleOff + 4 * (lane >> 4);
+#pragma unroll
+        for (int it = 0; it < kLatentIters; ++it) {
+            in.b8[it] = *reinterpret_cast<const uint2*>(raw + conv_raw + it * NW * kRow);
+            in.sc[it] = *reinterpret_cast<const float*>(raw + conv_scale + it * NW * kRow);
+        }
+    };
+    auto conv_store = [&](auto kr, auto kt, uint32_t vmask, const ConvIn& in, int i0, auto cnt, bool rope)
+        __attribute__((always_inline)) {
+        constexpr int KR = decltype(kr)::value;
+        constexpr int KT = decltype(kt)::value;
+        constexpr int CNT = decltype(cnt)::value;
+        const char* raw = raw_stage<KR>();
+        char* tile = tile_stage<KT>();
+#pragma unroll
+        for (int jj = 0; jj < CNT; ++jj) {
+            const int it = i0 + jj;
+            if (it < kLatentIters) {
+                const int r = it * NW + wave;  // wave-uniform
+                const uint4 d = dequant8(in.b8[it], in.sc[it]);
+                const bool keep = (vmask >> r) & 1u;
+                *reinterpret_cast<uint4*>(tile + r * kTileRow + ((lane ^ swz(r)) << 4)) =
+                    keep ? d : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        if (rope) {
+#pragma unroll
+            for (int it = 0; it < kRopeIters; ++it) {
+                const int n = it * 64 * NW + tid;
+                if (kRopeChunks % (64 * NW) == 0 || n < kRopeChunks) {
+                    const int r = n >> 3, k8 = n & 7;
+                    const uint4 d = *reinterpret_cast<const uint4*>(raw + r * kRow + kRopeOff + 16 * k8);
+                    const bool keep = (vmask >> r) & 1u;
+                    *reinterpret_cast<uint4*>(tile + r * kTileRow + ((64 + (k8 ^ swz(r))) << 4)) =
+                        keep ? d : make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
+        }
+    };
+
+    // Per-lane offsets pass through an empty asm statement at every step. The LDS objects span
+    // 160 KB, beyond the 64 KB immediate offset of the LDS instructions, so each (object, per-lane
+    // offset) pair would otherwise become its own long-lived register; recomputing costs one add.
+    auto refresh_offsets = [&]() __attribute__((always_inline)) {
+        asm volatile("" : "+v"(lane), "+v"(tid), "+v"(a_even), "+v"(a_odd));
+        asm volatile("" : "+v"(trbase[0]), "+v"(trbase[1]), "+v"(trbase[2]), "+v"(trbase[3]));
+#pragma unroll
+        for (int r = 0; r < R; ++r) asm volatile("" : "+v"(dma_kk[r]));
+    };
+
+    auto begin_segment = [&]() __attribute__((always_inline)) {
+        const uint16_t* qs = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)cc.s * Hq + head0 + (lane & 15)) * 576 +
+                             8 * (lane >> 4);
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) qr[ks] = *reinterpret_cast<const uint4*>(qs + 32 * ks);
+        // Wait for the queries inside this branch: otherwise the compiler waits for all vector-memory
+        // operations where the branch rejoins, which on every step would drain the row prefetch.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        m = kNegInf;
+        l = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < kDimTiles; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        seg_from_start = cc.k == 0;
+        if (seg_from_start && blockIdx.y == 0 && tid == 0) {
+            // This work-group holds the sequence's first unit: record which work-groups it spans.
+            p.seq_meta[2 * cc.s] = w;
+            p.seq_meta[2 * cc.s + 1] = (cc.g + cc.nu - 1) / per;
+        }
+    };
+
+    auto end_segment = [&]() __attribute__((always_inline)) {
+        const int c = lane & 15, g4 = lane >> 4;
+        const bool whole = seg_from_start && cc.k + 1 == cc.nu;
+        float L = l + __shfl_xor(l, 16);
+        L += __shfl_xor(L, 32);
+        // Output register j of a lane is head row 4 g4 + j; lane 4 g4 + j holds that row's (m, L).
+        float Lr[4], Mr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            Lr[j] = __shfl(L, 4 * g4 + j);
+            Mr[j] = __shfl(m, 4 * g4 + j);
+        }
+        const size_t row0 = (size_t)cc.s * Hq + head0 + 4 * g4;  // head row of register 0
+        if (whole) {
+            float inv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) inv[j] = Lr[j] > 0.f ? 1.f / Lr[j] : 0.f;
+            uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row0 * 512 + c;
+#pragma unroll
+            for (int dt = 0; dt < kDimTiles; ++dt) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j * 512 + 16 * (dt0 + dt)] = (uint16_t)(pack2<true>(O[dt][j] * inv[j], 0.f) & 0xFFFFu);
+                __builtin_amdgcn_sched_barrier(0);  // one tile at a time (see the rescale)
+            }
+        } else {
+            const size_t idx0 = row0 + (size_t)w * Hq;  // slot s + w
+            float* a = p.part_acc + idx0 * 512 + c;
+#pragma unroll
+            for (int dt = 0; dt < kDimTiles; ++dt) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[j * 512 + 16 * (dt0 + dt)] = O[dt][j];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (c == 0 && half == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<float2*>(p.part_ml + (idx0 + j) * 2) = make_float2(Mr[j], Lr[j]);
+            }
+        }
+    };
+
+    // Scores, online softmax and PV of the unit in tile stage KT (validity vi), with the
+    // dequantization of the next unit (raw stage KR2 -> tile stage KT2, validity vn) spread over the
+    // PV slots. Each slot loads the next slot's LDS operands, then issues its own products; the
+    // scheduling barriers keep the compiler from hoisting every operand load to the top, which would
+    // need more registers than the queries and outputs leave free.
+    auto compute = [&](auto kt, uint32_t vmask, auto kr2, auto kt2, uint32_t vn) __attribute__((always_inline)) {
+        constexpr int KT = decltype(kt)::value;
+        const char* tile = tile_stage<KT>();
+        const int g4 = lane >> 4;
+
+        // The dequantization of the next unit starts with its LDS reads, whose results are used
+        // during PV.
+        ConvIn cin;
+        conv_load(kr2, cin);
+
+        // Scores: 36 A operands (t, ks), loaded kPre products ahead; two accumulator chains (t = 0, 1).
+        constexpr int kPre = 4;
+        constexpr int kA = 2 * kKSteps;
+        f32x4_t S[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        auto load_a = [&](int x) __attribute__((always_inline)) {
+            const int ks = x >> 1, t = x & 1;
+            return *reinterpret_cast<const uint4*>(tile + ((ks & 1) ? a_odd : a_even) + t * kTile1 + (ks >> 1) * 128);
+        };
+        uint4 aring[kPre];
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) aring[i] = load_a(i);
+#pragma unroll
+        for (int x = 0; x < kA; ++x) {
+            const uint4 a = aring[x % kPre];
+            if (x + kPre < kA) aring[x % kPre] = load_a(x + kPre);
+            S[x & 1] = mfma_k32<true>(a, qr[x >> 1], S[x & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // Register j of tile t holds token 16t + g4 + 4j of head column c.
+        bool ok[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ok[t][j] = (vmask >> (16 * t + g4 + 4 * j)) & 1u;
+        float mx = kNegInf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mx = ok[t][j] ? fmaxf(mx, S[t][j]) : mx;
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float tmax = mx * sl2;
+        const bool need = tmax > m + kRescaleSlack;
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+            const float mnew = need ? tmax : m;
+            const float alpha = need ? fast_exp2(m - mnew) : 1.f;
+            l *= alpha;
+            m = mnew;
+            const f32x4_t av = {__shfl(alpha, 4 * g4), __shfl(alpha, 4 * g4 + 1), __shfl(alpha, 4 * g4 + 2),
+                                __shfl(alpha, 4 * g4 + 3)};
+            // One output tile at a time: the scheduling barriers keep the compiler from reading all 128
+            // accumulators into vector registers at once.
+#pragma unroll
+            for (int dt = 0; dt < kDimTiles; ++dt) {
+                O[dt] *= av;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            }
+        float pr[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float ex = fast_exp2(fmaf(S[t][j], sl2, -m));
+                pr[t][j] = ok[t][j] ? ex : 0.f;
+                l += pr[t][j];
+            }
+        const uint4 A = make_uint4(pack2<true>(pr[0][0], pr[0][1]), pack2<true>(pr[0][2], pr[0][3]),
+                                   pack2<true>(pr[1][0], pr[1][1]), pack2<true>(pr[1][2], pr[1][3]));
+
+        // PV: one 16-dim output tile per product; its B operand is two transposed reads (tile rows
+        // 0..15 and 16..31). The dequantization of the next unit is spread over eight groups of four.
+        constexpr int kGroups = kLatentIters < 8 ? kLatentIters : 8;
+        constexpr int kConvPerGroup = (kLatentIters + kGroups - 1) / kGroups;
+        constexpr int kTilesPerGroup = kDimTiles / kGroups;
+        const char* vtile = tile + half * (kDimTiles / 4) * 128;  // this wave's output dims
+        auto load_b = [&](int dt) __attribute__((always_inline)) {
+            const char* base = vtile + trbase[dt & 3] + (dt >> 2) * 128;
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(base));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(base + kTile1));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            return make_uint4(l2.x, l2.y, h2.x, h2.y);
+        };
+        uint4 bring[kPre];
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) bring[i] = load_b(i);
+#pragma unroll
+        for (int dt = 0; dt < kDimTiles; ++dt) {
+            const uint4 bop = bring[dt % kPre];
+            if (dt + kPre < kDimTiles) bring[dt % kPre] = load_b(dt + kPre);
+            O[dt] = mfma_k32<true>(A, bop, O[dt]);
+            if (dt % kTilesPerGroup == kTilesPerGroup - 1)
+                conv_store(kr2, kt2, vn, cin, (dt / kTilesPerGroup) * kConvPerGroup,
+                           std::integral_constant<int, kConvPerGroup>{}, dt == kDimTiles - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Step of unit u (K = u % 4): wait for unit u+1's rows, start loading unit u+4, compute unit u
+    // while dequantizing unit u+1. Returns false when the range is done.
+    auto step = [&](auto kst) __attribute__((always_inline)) -> bool {
+        constexpr int K = decltype(kst)::value;
+        prefetch_ids();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * RL));  // own loads of unit u+1 are done
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();                          // everyone's are; step u-1 is finished
+        compiler_fence();
+        const uint32_t cur = info[K];
+        const uint32_t nxt = info[(K + 1) & 3];
+        refresh_offsets();
+        issue(std::integral_constant<int, K>{});
+        if (__builtin_expect(cc.g == g_begin || cc.k == 0, 0)) begin_segment();
+        compute(std::integral_constant<int, K & 1>{}, cur, std::integral_constant<int, (K + 1) & 3>{},
+                std::integral_constant<int, (K + 1) & 1>{}, nxt);
+        if (__builtin_expect(cc.g + 1 == g_end || cc.k + 1 == cc.nu, 0)) end_segment();
+        advance(cc, p);
+        return cc.g < g_end;
+    };
+
+    // Prologue: units 0..3 in flight, unit 0 dequantized. The sparse form first copies the slot
+    // tables of units 0..3 and waits for them.
+    if constexpr (SPARSE) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) copy_slot_table();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        lds_barrier();
+    }
+    prefetch_ids();
+    issue(std::integral_constant<int, 0>{});
+    prefetch_ids();
+    issue(std::integral_constant<int, 1>{});
+    prefetch_ids();
+    issue(std::integral_constant<int, 2>{});
+    prefetch_ids();
+    issue(std::integral_constant<int, 3>{});
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * RL));
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    {
+        ConvIn cin;
+        conv_load(std::integral_constant<int, 0>{}, cin);
+        conv_store(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, info[0], cin, 0,
+                   std::integral_constant<int, kLatentIters>{}, true);
+    }
+
+    while (true) {
+        if (!step(std::integral_constant<int, 0>{})) break;
+        if (!step(std::integral_constant<int, 1>{})) break;
+        if (!step(std::integral_constant<int, 2>{})) break;
+        if (!step(std::integral_constant<int, 3>{})) break;
+    }
+    // Drain: the loads issued for units past the range still target this work-group's LDS.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+}
+
+}  // namespace pa

@@ -10,7 +10,7 @@
 //
 // Mapping: the rows of one K/V head are the (position, query head) pairs of the chunk,
 // position-major. A work-group owns 128 of them (4 waves x two 16-row tiles) and walks the paged
-// context in 64-token K/V tiles, which its waves copy from HBM straight into LDS (global_load_lds,
+// context in 64-token K/V tiles, which its waves copy from HBM straight into LDS (lds_dma,
 // two stages: the next tile is in flight while one is computed) and then share. Per tile and row
 // tile: S^T = K . Q^T on v_mfma_f32_16x16x32 (K from LDS, the rows' queries held in registers as the
 // B columns), causal and context masks, lazily rescaled online softmax, and O += P . V on
@@ -211,12 +211,8 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
                 const int64_t row_in_block = (j * kPT + dma_row[r]) & (bs - 1);
                 const char* ksrc = kb + row_in_block * krow + dma_chunk[r] * 16;
                 const char* vsrc = vb + row_in_block * vrow + dma_chunk[r] * 16;
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ksrc,
-                                                 (__attribute__((address_space(3))) void*)(ks_ + (16 * wave + 4 * r) * kPRow),
-                                                 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vsrc,
-                                                 (__attribute__((address_space(3))) void*)(vs_ + (16 * wave + 4 * r) * kPRow),
-                                                 16, 0, 0);
+                lds_dma<16>(ksrc, lds_addr(ks_) + (16 * wave + 4 * r) * kPRow);
+                lds_dma<16>(vsrc, lds_addr(vs_) + (16 * wave + 4 * r) * kPRow);
             }
         } else {
             // No context tokens here, or an invalid block id: the scores are masked; the value rows

@@ -532,17 +532,23 @@ void decode_mla_kernel(MlaDecodeParams p) {
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // Register j of tile t holds token 16t + g4 + 4j of head column c.
-        bool ok[2][4];
+        // Register j of tile t holds token 16t + g4 + 4j of head column c. Rows past the unit's valid
+        // ones (in the last unit of a sequence, or in an invalid block) are masked out; a whole unit,
+        // the usual case, takes the branch without the masks (vmask is wave-uniform).
+        const bool whole_unit = vmask == 0xFFFFFFFFu;
+        auto row_ok = [&](auto masked, int t, int j) __attribute__((always_inline)) -> bool {
+            if constexpr (decltype(masked)::value) return (vmask >> (16 * t + g4 + 4 * j)) & 1u;
+            else return true;
+        };
+        auto unit_max = [&](auto masked) __attribute__((always_inline)) {
+            float mx = kNegInf;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ok[t][j] = (vmask >> (16 * t + g4 + 4 * j)) & 1u;
-        float mx = kNegInf;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) mx = ok[t][j] ? fmaxf(mx, S[t][j]) : mx;
+                for (int j = 0; j < 4; ++j) mx = row_ok(masked, t, j) ? fmaxf(mx, S[t][j]) : mx;
+            return mx;
+        };
+        float mx = whole_unit ? unit_max(std::false_type{}) : unit_max(std::true_type{});
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float tmax = mx * sl2;
@@ -554,23 +560,27 @@ void decode_mla_kernel(MlaDecodeParams p) {
             m = mnew;
             const f32x4_t av = {__shfl(alpha, 4 * g4), __shfl(alpha, 4 * g4 + 1), __shfl(alpha, 4 * g4 + 2),
                                 __shfl(alpha, 4 * g4 + 3)};
-            // One output tile at a time: the scheduling barriers keep the compiler from reading all 128
-            // accumulators into vector registers at once.
+            // One output tile at a time: the scheduling barriers keep the compiler from reading every
+            // output into fresh registers at once.
 #pragma unroll
             for (int dt = 0; dt < kDimTiles; ++dt) {
                 O[dt] *= av;
                 __builtin_amdgcn_sched_barrier(0);
             }
-            }
+        }
         float pr[2][4];
+        auto unit_exp = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float ex = fast_exp2(fmaf(S[t][j], sl2, -m));
-                pr[t][j] = ok[t][j] ? ex : 0.f;
-                l += pr[t][j];
-            }
+                for (int j = 0; j < 4; ++j) {
+                    const float ex = fast_exp2(fmaf(S[t][j], sl2, -m));
+                    pr[t][j] = row_ok(masked, t, j) ? ex : 0.f;
+                    l += pr[t][j];
+                }
+        };
+        if (whole_unit) unit_exp(std::false_type{});
+        else unit_exp(std::true_type{});
         const uint4 A = make_uint4(pack2<true>(pr[0][0], pr[0][1]), pack2<true>(pr[0][2], pr[0][3]),
                                    pack2<true>(pr[1][0], pr[1][1]), pack2<true>(pr[1][2], pr[1][3]));
 

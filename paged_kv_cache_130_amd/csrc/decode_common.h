@@ -68,6 +68,13 @@ __device__ __forceinline__ void lds_dma(const void* src, uint32_t lds) {
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory");
 }
 
+// Two E4M3 codes (bytes 0, 1 of w, or bytes 2, 3 when HI) -> two bf16 in one dword, the first in the
+// low half. Exact: every E4M3 value is a bf16 value, and the scale is 1.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // v_perm_b32 selectors: low 16-bit halves of (a, b) -> (a.lo, b.lo); high halves -> (a.hi, b.hi).
 constexpr uint32_t kSelLo = 0x05040100u;
 constexpr uint32_t kSelHi = 0x07060302u;

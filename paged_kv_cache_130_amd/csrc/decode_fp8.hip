@@ -12,7 +12,8 @@
 //  * A lane holds 16 bytes = 16 values of one row: LPR = D/16 lanes cover a head's row, and one
 //    wave-wide 16-byte load covers RPL = 64/LPR rows. Half the bytes of a 16-bit cache per token.
 //  * v_cvt_pk_f32_fp8 turns two codes into two exact fp32 values. Every E4M3 value is exactly a
-//    bf16 value too (4 significant bits, exponents -9..8), so K goes on as bf16 pairs into
+//    bf16 value too (4 significant bits, exponents -9..8), so K goes on as bf16 pairs (two codes per
+//    v_cvt_scalef32_pk_bf16_fp8 with scale 1) into
 //    v_dot2_f32_bf16 against the bf16 query (exact products, fp32 sums), and V as fp32 into fp32
 //    multiply-adds with the fp32 probabilities (no rounding of p).
 //  * The scales are applied outside the loops: K's scale is folded into the softmax scale, and V's
@@ -44,15 +45,13 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* o) {
     o[3] = b.y;
 }
 
-// 16 codes -> 8 bf16 pairs (exact: an E4M3 value's fp32 form has its low 16 bits zero).
+// 16 codes -> 8 bf16 pairs (exact).
 __device__ __forceinline__ void e4m3x16_to_bf16x2(const uint4& w, uint32_t (&o)[8]) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float f[4];
-        e4m3x4_to_f32(ws[i], f);
-        o[2 * i] = __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), kSelHi);
-        o[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), kSelHi);
+        o[2 * i] = e4m3x2_bf16<false>(ws[i]);
+        o[2 * i + 1] = e4m3x2_bf16<true>(ws[i]);
     }
 }
 

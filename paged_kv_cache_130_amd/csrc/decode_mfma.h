@@ -91,19 +91,12 @@ __device__ __forceinline__ void mfma_tile_step(const uint4 (&kk)[4], uint4 (&vv)
     }
 }
 
-typedef float f32x2_dm_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2_dm_t __attribute__((ext_vector_type(2)));
 
-// 8 E4M3 codes -> 8 bf16 values (exact: an E4M3 value's fp32 form has its low 16 bits zero).
+// 8 E4M3 codes -> 8 bf16 values (exact).
 __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 w) {
-    const f32x2_dm_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false);
-    const f32x2_dm_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
-    const f32x2_dm_t c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false);
-    const f32x2_dm_t d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
-    auto hi2 = [](float x0, float x1) __attribute__((always_inline)) {
-        return __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), kSelHi);
-    };
-    return make_uint4(hi2(a.x, a.y), hi2(b.x, b.y), hi2(c.x, c.y), hi2(d.x, d.y));
+    return make_uint4(e4m3x2_bf16<false>(w.x), e4m3x2_bf16<true>(w.x), e4m3x2_bf16<false>(w.y),
+                      e4m3x2_bf16<true>(w.y));
 }
 
 __device__ __forceinline__ uint2 load_nt8(const char* ptr) {

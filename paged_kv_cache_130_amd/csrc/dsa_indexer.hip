@@ -42,12 +42,6 @@ constexpr int kQRow = 128 * 2 + 16;             // LDS row of one query head (pa
 
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
-// Two e4m3 codes (bytes 0, 1 or 2, 3 of w) -> two bf16 (exact: every e4m3 value is a bf16 value).
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-}
-
 __device__ __forceinline__ uint4 codes8_bf16(uint32_t lo, uint32_t hi) {
     return make_uint4(e4m3x2_bf16<false>(lo), e4m3x2_bf16<true>(lo), e4m3x2_bf16<false>(hi),
                       e4m3x2_bf16<true>(hi));

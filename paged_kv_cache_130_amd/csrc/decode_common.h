@@ -56,16 +56,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // (lgkmcnt(0)), which in a pipeline that always has copies in flight defeats every operand prefetch.
 // Hidden from the compiler, the copy is ordered only by the caller: an s_waitcnt vmcnt for its own
 // copies, then a barrier, before anything reads the destination, and an s_waitcnt vmcnt(0) before
-// the kernel ends. M0 (which the instruction takes the LDS address from) is set inside the asm; the
-// kernels that use this helper use M0 for nothing else.
+// the kernel ends. M0 (which the instruction takes the LDS address from) is set inside the asm, one
+// wait state ahead of the copy (an SALU write of M0 followed by a global load into LDS needs one, as
+// the compiler also inserts for the builtin); the kernels that use this helper use M0 for nothing else.
 template <int BYTES>
 __device__ __forceinline__ void lds_dma(const void* src, uint32_t lds) {
     static_assert(BYTES == 4 || BYTES == 16, "4 or 16 bytes per lane");
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
     if constexpr (BYTES == 16)
-        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
     else
-        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory");
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory");
 }
 
 // Two E4M3 codes (bytes 0, 1 of w, or bytes 2, 3 when HI) -> two bf16 in one dword, the first in the

@@ -193,7 +193,7 @@ __device__ __forceinline__ void merge_partials(const float* ml, int64_t ml_strid
                                                int64_t acc_stride, int n, uint16_t* out) {
     constexpr int DPL = D / 64;            // output values per lane
     constexpr int U = 16;                  // partials per unrolled step
-    constexpr int P = D >= 512 ? 4 : 16;   // partials loaded before their weights are known
+    constexpr int P = D >= 512 ? 4 : 8;    // partials loaded before their weights are known
     const int lane = threadIdx.x & 63;
     const float* ap = acc + lane * DPL;
     // The first P partials' accumulators go out with the (m, l) loads, so that the common case (at

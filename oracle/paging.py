@@ -104,8 +104,3 @@ def block_outer_views(caches, block_size: int):
         views[name] = CacheView(offset=base, layer_stride=page, block_stride=block_total, row_bytes=row)
         base += nl * page
     return views, block_total
-
-
-def view_extent(view: CacheView, layer: int, num_blocks: int, block_size: int) -> int:
-    """One past the last byte that rows of `layer` can touch through this view."""
-    return address(view, layer, num_blocks - 1, block_size - 1) + view.row_bytes

@@ -110,7 +110,7 @@ __device__ __forceinline__ int query_row(int s, const DenseDecodeParams& p) {
 // Work item w of the partition-major list -> (sequence, partition). Returns false past the end.
 // C(q) = sum_s min(nparts(s), q) counts the items of partitions below q; item w lies in the partition
 // p with C(p) <= w < C(p+1), and is the (w - C(p))-th sequence (in order) that has more than p
-// partitions. Counts stay far below 2^24, so the float reductions are exact.
+// partitions. The counts are summed as integers (the host bounds num_seqs * max_parts below 2^31).
 //
 // With up to 256 sequences the partition counts of all of them are read once into registers
 // (sequence 64k + lane in register k), with every load issued before the first wait, so the search
@@ -147,7 +147,7 @@ __device__ __forceinline__ bool find_work(int w, const DenseDecodeParams& p, int
         } else {
             for (int s = lane; s < p.num_seqs; s += 64) c += min(parts_of(s, p), cap);
         }
-        return __builtin_amdgcn_readfirstlane((int)group_sum<64>((float)c));
+        return __builtin_amdgcn_readfirstlane(wave_sum_int(c));
     };
     if (w >= count_below(p.max_parts)) return false;
     int lo = 0, hi = p.max_parts;  // C(lo) <= w < C(hi)

@@ -36,6 +36,17 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Integer sum over the 64 lanes of the wave (exact; every lane gets the sum).
+__device__ __forceinline__ int wave_sum_int(int x) {
+    x += __builtin_amdgcn_mov_dpp(x, kDppQuadXor1, 0xF, 0xF, true);
+    x += __builtin_amdgcn_mov_dpp(x, kDppQuadXor2, 0xF, 0xF, true);
+    x += __builtin_amdgcn_mov_dpp(x, kDppRowHalfMirror, 0xF, 0xF, true);
+    x += __builtin_amdgcn_mov_dpp(x, kDppRowMirror, 0xF, 0xF, true);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 2-element dot product with fp32 accumulation (v_dot2_f32_f16 / v_dot2_f32_bf16).

@@ -90,6 +90,10 @@ SHAPES = [
     ("bf16", 32, 8, 128, 16, [2, 3, 4, 5, 6, 7, 8, 9], 0),
     ("bf16", 8, 8, 128, 16, [2, 3, 4, 5], 0),
     ("bf16", 8, 8, 64, 16, [2, 3, 5], 0),
+    # partitions of 16 tokens: more than 64 (and more than 128) partials per row to merge
+    ("bf16", 8, 2, 128, 16, [1100, 2100, 3, 0], 16),
+    ("f16", 4, 4, 128, 16, [1300, 2, 1025], 16),
+    ("bf16", 4, 4, 256, 16, [1040, 17], 16),
 ]
 
 
@@ -146,6 +150,28 @@ def test_shared_prefix_equals_copied_prefix_bitwise():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv,num_seqs,part", [
+    ("f16", 2, 2, 400, 0),      # vector kernel
+    ("bf16", 8, 2, 300, 128),   # matrix-core kernel (group 4)
+    ("bf16", 16, 1, 600, 0),    # matrix-core kernel (group 16)
+])
+def test_decode_many_sequences(dtype, Hq, Hkv, num_seqs, part):
+    """More than 256 sequences: the work search re-reads the partition counts from memory.
+
+    Contexts are drawn in [0, 1200] with empty and one-token sequences forced in, so items of every
+    partition index exist beside sequences with a single (or an empty) item.
+    """
+    rng = np.random.default_rng(num_seqs + Hq)
+    ctx = rng.integers(0, 1201, size=num_seqs)
+    ctx[[0, 7, num_seqs - 1]] = 0
+    ctx[[1, 130, 257, num_seqs - 2]] = 1
+    ctx[[2, 299]] = 1200
+    need = sum(P.blocks_needed(int(n), 16) for n in ctx)
+    case = workloads.make_dense_case("tiny", seed=4500 + num_seqs, context_lens=ctx.tolist(), num_blocks=need + 9,
+                                     num_q_heads=Hq, num_kv_heads=Hkv, dtype=dtype)
+    run_case(case, part)
+
+
 # --------------------------------------------------------------------------
 # Full-size workloads, in the launch configuration the bench times (library-chosen
 # partition), checked on sampled (sequence, head) outputs.
@@ -181,6 +207,11 @@ def test_full_size_mha13b_sampled():
 def test_full_size_gqa_shared_prefix_sampled():
     """256 seqs sharing a 2000-token prompt plus lognormal suffixes, 32/8 heads, bf16."""
     sampled_full_size(workloads.make_dense_case("gqa_prefix", device="cuda"), 12, 2)
+
+
+def test_full_size_gqa_copied_prefix_sampled():
+    """The same batch with each sequence's 125 prompt blocks copied to private blocks (the timed variant)."""
+    sampled_full_size(workloads.make_dense_case("gqa_prefix", device="cuda", copied_prefix=True), 12, 3)
 
 
 def test_full_size_long_context_decode_sampled():

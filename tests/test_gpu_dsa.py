@@ -247,21 +247,35 @@ def test_full_size_dsa_sparse_sampled():
             mask = np.zeros(n, dtype=bool)
             mask[sel] = True
             assert (want[mask] + tol[mask]).min() >= (want[~mask] - tol[~mask]).max(), f"seq {b}: invalid top-k"
-    got = sparse_decode(case, img, layer, slots, lens, top_k)
-    assert np.isfinite(got).all()
-    q = bits_np(case.q)
     mla_rows = seq_rows(case, layer, "mla")
-    for b in sampled:
-        # A compact image of the sequence's rows in position order (block j = positions 64j..),
-        # addressed by position: the oracle reads generator rows, not the device cache.
-        n = int(case.context_lens[b])
-        rows = mla_rows[b].cpu().numpy()
-        nb = P.blocks_needed(n, bs)
-        image = np.zeros(nb * bs * 656, dtype=np.uint8)
-        image[:n * 656] = rows.reshape(-1)
-        view = P.CacheView(0, 0, bs * 656, 656)
-        want = D.sparse_mla_decode(q[b:b + 1], image, view, 0, [pos[b, :lens[b]]], bs, nb, case.scale)
-        assert_close(got[b], want[0], MLA_ATOL, MLA_RTOL, f"seq {b} (ctx {n})")
+    q_plain = case.q
+    # The second pass scales the queries by 6 so each head's softmax over the 2048 selected rows
+    # concentrates and the outputs reach |o| ~ 0.3-1, where the 3e-2 tolerance discriminates.
+    for gain in (1.0, 6.0):
+        case.q = q_plain if gain == 1.0 else (q_plain.view(torch.bfloat16).float() * gain).to(
+            torch.bfloat16).view(torch.int16)
+        got = sparse_decode(case, img, layer, slots, lens, top_k)
+        assert np.isfinite(got).all()
+        q = bits_np(case.q)
+        for b in sampled:
+            # A compact image of the sequence's rows in position order (block j = positions 64j..),
+            # addressed by position: the oracle reads generator rows, not the device cache.
+            n = int(case.context_lens[b])
+            rows = mla_rows[b].cpu().numpy()
+            nb = P.blocks_needed(n, bs)
+            image = np.zeros(nb * bs * 656, dtype=np.uint8)
+            image[:n * 656] = rows.reshape(-1)
+            view = P.CacheView(0, 0, bs * 656, 656)
+            want = D.sparse_mla_decode(q[b:b + 1], image, view, 0, [pos[b, :lens[b]]], bs, nb, case.scale)
+            assert_close(got[b], want[0], MLA_ATOL, MLA_RTOL, f"gain {gain} seq {b} (ctx {n})")
+            if gain != 1.0 and b == sampled[0]:
+                # An all-zero output, or scores without RoPE, would fail this check.
+                q_nr = q[b:b + 1].copy()
+                q_nr[..., 512:] = 0
+                want_nr = D.sparse_mla_decode(q_nr, image, view, 0, [pos[b, :lens[b]]], bs, nb, case.scale)
+                bound = MLA_ATOL + MLA_RTOL * np.abs(want[0])
+                assert (np.abs(want[0]) > bound).mean() > 0.9
+                assert (np.abs(want_nr[0] - want[0]) > bound).mean() > 0.6
 
 
 def test_many_sequences_and_uncached_block_ids():

@@ -90,6 +90,8 @@ SHAPES = [
     (8, 8, 64, 16, [2, 3, 5], 0),
     (32, 2, 128, 16, [7, 300, 1100], 0),      # group 16, matrix cores
     (24, 8, 128, 16, [2, 3, 4, 5, 33], 0),    # group 3, matrix cores, short rows
+    (8, 2, 128, 16, [1100, 2100, 1, 0], 16),  # more than 64 and 128 partials per row, matrix cores
+    (4, 4, 128, 16, [1300, 3, 1025], 16),     # more than 64 partials, vector kernel
 ]
 
 
@@ -101,6 +103,21 @@ def test_fp8_write_and_decode(Hq, Hkv, D, bs, ctx, part):
     k8, v8 = quantize_pool(case)
     poison(k8, v8, case)
     decode(case, k8, v8, part)
+
+
+@pytest.mark.parametrize("Hq,Hkv,num_seqs", [(2, 2, 350), (8, 2, 520)])
+def test_fp8_many_sequences(Hq, Hkv, num_seqs):
+    """More than 256 sequences (the work search re-reads the partition counts), empty and 1-token rows."""
+    rng = np.random.default_rng(num_seqs)
+    ctx = rng.integers(0, 900, size=num_seqs)
+    ctx[[0, num_seqs - 1]] = 0
+    ctx[[1, 260, num_seqs - 2]] = 1
+    need = sum(P.blocks_needed(int(n), 16) for n in ctx)
+    case = workloads.make_dense_case("tiny", seed=5600 + num_seqs, context_lens=ctx.tolist(), num_blocks=need + 5,
+                                     num_q_heads=Hq, num_kv_heads=Hkv, dtype="bf16")
+    k8, v8 = quantize_pool(case)
+    poison(k8, v8, case)
+    decode(case, k8, v8, 0)
 
 
 def test_fp8_write_from_f16_sources():

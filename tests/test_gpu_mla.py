@@ -94,6 +94,7 @@ MLA_SHAPES = [
     (128, 128, [127, 128, 129, 1000, 3, 0], 0),
     (128, 64, [1, 2, 3, 700, 64, 65], 32),
     (48, 256, [255, 256, 257, 40], 96),
+    (16, 16, [3000, 5, 2100], 32),      # one unit per work-group: 94 partials of one row to merge
 ]
 
 
@@ -123,6 +124,24 @@ def test_mla_decode_is_deterministic():
     assert torch.equal(a, b)
 
 
+def scaled_queries(q, factor):
+    """bf16 query bits times `factor`, rounded to bf16 (the oracle reads the stored bits)."""
+    return (q.view(torch.bfloat16).float() * factor).to(torch.bfloat16).view(torch.int16)
+
+
+def assert_discriminating(ref, ref_without_rope, what):
+    """The check at the MLA tolerance would catch an all-zero output and a score that drops RoPE."""
+    zero_fails = np.abs(ref) > MLA_ATOL + MLA_RTOL * np.abs(ref)
+    rope_fails = np.abs(ref_without_rope - ref) > MLA_ATOL + MLA_RTOL * np.abs(ref)
+    assert zero_fails.mean() > 0.9, f"{what}: an all-zero output would pass {1 - zero_fails.mean():.0%} of elements"
+    assert rope_fails.mean() > 0.6, f"{what}: dropping RoPE would pass {1 - rope_fails.mean():.0%} of elements"
+
+
+# Queries scaled by 6 make each head's softmax concentrate on a few tokens (score spread about 6
+# instead of 1), so outputs reach |o| ~ 0.3-1 at contexts of 1K-8K and the 3e-2 tolerance discriminates.
+QUERY_GAIN = 6.0
+
+
 def test_full_size_dsa_mla_sampled():
     """64 seqs, ctx U[1024, 8192], 128 heads on one latent head, 2 layers, 9216 blocks x 100864 B."""
     case = workloads.make_mla_case(device="cuda")
@@ -137,17 +156,27 @@ def test_full_size_dsa_mla_sampled():
             assert np.array_equal(got, case.mla_rows[layer][t].cpu().numpy())
             a = P.address(idx_v, layer, b, pos)
             assert np.array_equal(img.view(-1)[a:a + 132].cpu().numpy(), case.idx_rows[layer][t].cpu().numpy())
-    q = bits_np(case.q)
     rng = np.random.default_rng(5)
     seqs = sorted(set(rng.choice(64, size=5, replace=False).tolist()) | {int(np.argmax(case.context_lens))})
-    for layer in range(2):
-        out = mla_decode_gpu(case, img, layer)
-        got = out.view(torch.bfloat16).double().cpu().numpy()
-        assert np.isfinite(got).all()
-        for s in seqs:
-            n = int(case.context_lens[s])
-            nblk = P.blocks_needed(n, BS)
-            ids = torch.as_tensor(case.block_tables[s, :nblk].astype(np.int64), device="cuda")
-            sub = image_of(img.index_select(0, ids))
-            ref = A.mla_decode(q[s:s + 1], sub, mla_v, layer, np.arange(nblk)[None, :], [n], BS, case.scale)
-            assert_close(got[s], ref[0], MLA_ATOL, MLA_RTOL, f"layer {layer} seq {s} (ctx {n})")
+    q_plain = case.q
+    for gain in (1.0, QUERY_GAIN):
+        case.q = q_plain if gain == 1.0 else scaled_queries(q_plain, gain)
+        q = bits_np(case.q)
+        for layer in range(2):
+            out = mla_decode_gpu(case, img, layer)
+            got = out.view(torch.bfloat16).double().cpu().numpy()
+            assert np.isfinite(got).all()
+            for s in seqs:
+                n = int(case.context_lens[s])
+                nblk = P.blocks_needed(n, BS)
+                ids = torch.as_tensor(case.block_tables[s, :nblk].astype(np.int64), device="cuda")
+                sub = image_of(img.index_select(0, ids))
+                tbl = np.arange(nblk)[None, :]
+                ref = A.mla_decode(q[s:s + 1], sub, mla_v, layer, tbl, [n], BS, case.scale)
+                what = f"gain {gain} layer {layer} seq {s} (ctx {n})"
+                assert_close(got[s], ref[0], MLA_ATOL, MLA_RTOL, what)
+                if gain != 1.0 and s == seqs[0]:
+                    q_norope = q[s:s + 1].copy()
+                    q_norope[..., 512:] = 0
+                    ref_nr = A.mla_decode(q_norope, sub, mla_v, layer, tbl, [n], BS, case.scale)
+                    assert_discriminating(ref[0], ref_nr[0], what)

@@ -1,5 +1,4 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each one.
-import os, sys; sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 
 Each mutation patches one oracle function for the duration of the test. A
 pin that still passes under the mutation would be a pin that cannot see that

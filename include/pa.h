@@ -111,8 +111,13 @@ typedef struct pa_attn_desc {
     int32_t v_dim;                /* dense: == qk_dim. MLA: 512 */
     int32_t block_size;           /* tokens per block: a power of two from 16 to 256 */
     int32_t layer;                /* layer index applied to the views' layer_stride */
-    int32_t partition_size;       /* decode only: tokens per split-context partition; 0 lets the
-                                     library choose; otherwise a positive multiple of block_size */
+    int32_t partition_size;       /* decode only: tokens per split-context partition, a positive
+                                     multiple of block_size (at most 64 blocks are used); 0 lets the
+                                     library choose from the item count estimate
+                                     num_kv_heads*num_seqs*ceil(max_context_len/P): 1024 tokens if
+                                     it reaches 8192, else the largest of 768, 512 reaching 2048,
+                                     else 256 (whole blocks). For the MLA format: tokens per
+                                     work-group range, a multiple of 32 */
     int64_t num_blocks;           /* physical blocks addressable through the views */
     pa_cache_view k_view;         /* K rows (MLA: the 656-byte rows) */
     pa_cache_view v_view;         /* V rows (dense only; ignored for MLA) */

@@ -59,7 +59,7 @@ class PagedAttentionError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_130_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_130_amd/build.py`")
     # torch ships its own HIP runtime under the same soname (libamdhip64.so.7). Loading torch first
     # makes libpa.so bind to that runtime, so the streams and device memory torch hands over belong to
     # the runtime that launches the kernels. Loading libpa.so first would pull a second runtime into the

@@ -1,6 +1,6 @@
 """Build libpa.so (the HIP kernels and the C ABI of include/pa.h) in-tree for gfx950.
 
-    python -m paged_kv_cache_130_amd.build
+    python paged_kv_cache_130_amd/build.py      (a script: importing the package would load the old library)
 
 Each source is compiled by hipcc into _build/ in parallel, then linked into
 paged_kv_cache_130_amd/libpa.so, which the ctypes binding loads.

@@ -107,22 +107,48 @@ __device__ __forceinline__ int query_row(int s, const DenseDecodeParams& p) {
     return p.query_start_loc != nullptr ? __builtin_amdgcn_readfirstlane(p.query_start_loc[s]) : s;
 }
 
-// Work item w of the partition-major list -> (sequence, partition). Returns false past the end.
-// C(q) = sum_s min(nparts(s), q) counts the items of partitions below q; item w lies in the partition
-// p with C(p) <= w < C(p+1), and is the (w - C(p))-th sequence (in order) that has more than p
-// partitions. The counts are summed as integers (the host bounds num_seqs * max_parts below 2^31).
+// Work item w of the list -> (sequence, partition, clamped context length). Returns false past
+// the end.
 //
-// With up to 256 sequences the partition counts of all of them are read once into registers
+// The list holds every full partition (partition_tokens tokens) first, in partition-major order,
+// then one item per sequence for its last, partial partition (or for its empty context, which
+// writes the zero output), ordered by decreasing length in 8 buckets of partition_tokens / 8
+// tokens (empty contexts last) and by sequence within a bucket. Waves take items in list order, so
+// items of equal length run together and the short ones run last: the waves of the call finish
+// close together instead of waiting on a few full partitions dispatched at the end. (Partition
+// boundaries depend only on logical positions, so the order changes no result.)
+//
+// Full part: C(q) = sum_s min(f_s, q), f_s = full partitions of s, counts the full items of
+// partitions below q; item w lies in partition q with C(q) <= w < C(q+1) and is the (w - C(q))-th
+// sequence (in order) with more than q full partitions. Partial part: bucket counts from the
+// longest bucket down. Counts are summed as integers (the host bounds num_seqs * max_parts below
+// 2^31).
+//
+// With up to 256 sequences the per-sequence values of all of them are read once into registers
 // (sequence 64k + lane in register k), with every load issued before the first wait, so the search
-// costs one memory round trip and then only register arithmetic. With more sequences the counts
-// are re-read for every step of the search.
-__device__ __forceinline__ bool find_work(int w, const DenseDecodeParams& p, int& s_out, int& part_out) {
+// costs one memory round trip and then only register arithmetic. With more sequences they are
+// re-read from memory for every count.
+__device__ __forceinline__ bool find_work(int w, const DenseDecodeParams& p, int& s_out, int& part_out, int& ctx_out) {
     constexpr int NC = 4;
+    constexpr int kBuckets = 8;
     const int lane = threadIdx.x & 63;
     const bool fast = p.num_seqs <= 64 * NC;
-    int pv[NC];
+    const bool mixed = p.query_start_loc != nullptr;
+    const int P = p.partition_tokens;
+    // Full partitions of sequence s, and the key of its partial item: 1 + bucket for a partial
+    // partition of r tokens (bucket (r - 1) * 8 / P), 0 for an empty context, -1 for none.
+    auto seq_info = [&](int ctx_raw, bool takes_part, int& full, int& key, int& ctx) __attribute__((always_inline)) {
+        ctx = clamp_context(ctx_raw, p);
+        const int r = ctx % P;
+        full = takes_part ? ctx / P : 0;
+        key = !takes_part ? -1 : r > 0 ? 1 + ((r - 1) * kBuckets) / P : (ctx == 0 ? 0 : -1);
+    };
+    auto mem_info = [&](int s, int& full, int& key, int& ctx) __attribute__((always_inline)) {
+        const bool takes = !mixed || p.query_start_loc[s + 1] - p.query_start_loc[s] == 1;
+        seq_info(p.context_lens[s], takes, full, key, ctx);
+    };
+    int fv[NC], kv[NC], cv[NC];
     if (fast) {
-        const bool mixed = p.query_start_loc != nullptr;
         const int32_t* qsl = mixed ? p.query_start_loc : p.context_lens;  // any valid address if not mixed
         int cl[NC], q0[NC], q1[NC];
 #pragma unroll
@@ -134,50 +160,81 @@ __device__ __forceinline__ bool find_work(int w, const DenseDecodeParams& p, int
         }
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
-            const int ctx = clamp_context(cl[k], p);
-            const int n = ctx == 0 ? 1 : (ctx + p.partition_tokens - 1) / p.partition_tokens;
-            pv[k] = (64 * k + lane < p.num_seqs && (!mixed || q1[k] - q0[k] == 1)) ? n : 0;
+            const bool takes = 64 * k + lane < p.num_seqs && (!mixed || q1[k] - q0[k] == 1);
+            seq_info(cl[k], takes, fv[k], kv[k], cv[k]);
         }
     }
-    auto count_below = [&](int cap) __attribute__((always_inline)) {
+    // Sum over sequences of f(full, key).
+    auto count = [&](auto f) __attribute__((always_inline)) {
         int c = 0;
         if (fast) {
 #pragma unroll
-            for (int k = 0; k < NC; ++k) c += min(pv[k], cap);
+            for (int k = 0; k < NC; ++k) c += f(fv[k], kv[k]);
         } else {
-            for (int s = lane; s < p.num_seqs; s += 64) c += min(parts_of(s, p), cap);
+            for (int s = lane; s < p.num_seqs; s += 64) {
+                int full, key, ctx;
+                mem_info(s, full, key, ctx);
+                c += f(full, key);
+            }
         }
         return __builtin_amdgcn_readfirstlane(wave_sum_int(c));
     };
-    if (w >= count_below(p.max_parts)) return false;
-    int lo = 0, hi = p.max_parts;  // C(lo) <= w < C(hi)
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (count_below(mid) <= w) lo = mid;
-        else hi = mid;
-    }
-    int r = w - count_below(lo);  // rank among sequences with more than lo partitions
-    for (int base = 0; base < p.num_seqs; base += 64) {
-        const int s = base + lane;
-        int n = 0;
-        if (fast) {
+    // The r-th sequence (in order) for which pred(full, key) holds; its full count and context in
+    // full_out and ctx_out.
+    auto nth = [&](int r, auto pred, int& s_found, int& full_out) __attribute__((always_inline)) -> bool {
+        for (int base = 0; base < p.num_seqs; base += 64) {
+            const int s = base + lane;
+            int full = 0, key = -1, ctx = 0;
+            if (fast) {
 #pragma unroll
-            for (int k = 0; k < NC; ++k) n = (base >> 6) == k ? pv[k] : n;
-        } else {
-            n = s < p.num_seqs ? parts_of(s, p) : 0;
+                for (int k = 0; k < NC; ++k)
+                    if ((base >> 6) == k) {
+                        full = fv[k];
+                        key = kv[k];
+                        ctx = cv[k];
+                    }
+            } else if (s < p.num_seqs) {
+                mem_info(s, full, key, ctx);
+            }
+            const bool has = s < p.num_seqs && pred(full, key);
+            const uint64_t mask = __builtin_amdgcn_ballot_w64(has);
+            const int cnt = __builtin_popcountll(mask);
+            if (r < cnt) {
+                const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                const uint64_t hit = __builtin_amdgcn_ballot_w64(has && below == r);
+                const int lh = __builtin_ctzll(hit);
+                s_found = base + lh;
+                full_out = __builtin_amdgcn_readlane(full, lh);
+                ctx_out = __builtin_amdgcn_readlane(ctx, lh);
+                return true;
+            }
+            r -= cnt;
         }
-        const bool has = n > lo;
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(has);
-        const int cnt = __builtin_popcountll(mask);
-        if (r < cnt) {
-            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(has && below == r);
-            s_out = base + __builtin_ctzll(hit);
-            part_out = lo;
+        return false;
+    };
+    int full_of_s = 0;
+    const int F = count([&](int full, int) { return min(full, p.max_parts); });
+    if (w < F) {
+        int lo = 0, hi = p.max_parts;  // C(lo) <= w < C(hi)
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (count([&](int full, int) { return min(full, mid); }) <= w) lo = mid;
+            else hi = mid;
+        }
+        const int r = w - count([&](int full, int) { return min(full, lo); });
+        part_out = lo;
+        return nth(r, [&](int full, int) { return full > lo; }, s_out, full_of_s);
+    }
+    int r = w - F;
+    for (int key = kBuckets; key >= 0; --key) {
+        const int c = count([&](int, int k) { return k == key ? 1 : 0; });
+        if (r < c) {
+            if (!nth(r, [&](int, int k) { return k == key; }, s_out, full_of_s)) return false;
+            part_out = full_of_s;
             return true;
         }
-        r -= cnt;
+        r -= c;
     }
     return false;
 }

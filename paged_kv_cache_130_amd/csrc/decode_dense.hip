@@ -147,15 +147,14 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
     const int r = lane / LPR;
     const int c = lane % LPR;
 
-    // Compact, partition-major work list: (partition p, sequence s) pairs with p < nparts(s), ordered by p
-    // then s, and the KV head fastest. Full-length partitions are dispatched first and the ragged tails
-    // of long sequences last, with no empty slots in between; waves past the end exit at once.
+    // Work list (find_work): full partitions partition-major, then each sequence's partial partition
+    // from the longest to the shortest, with the KV head fastest; waves past the end exit at once.
     const int item = blockIdx.x * 4 + wave;
     const int kvh = item % p.num_kv_heads;
     int s, part;
-    if (!find_work(item / p.num_kv_heads, p, s, part)) return;
+    int ctx;
+    if (!find_work(item / p.num_kv_heads, p, s, part, ctx)) return;
     const int bs = p.block_size;
-    const int ctx = clamp_context(__builtin_amdgcn_readfirstlane(p.context_lens[s]), p);
     const int P = p.partition_tokens;
     const int nparts = (ctx + P - 1) / P;
     const int hq0 = kvh * G;  // first query head of this group

@@ -136,9 +136,9 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(DenseDecodeParams p) {
     const int item = blockIdx.x * 4 + wave;
     const int kvh = item % p.num_kv_heads;
     int s, part;
-    if (!find_work(item / p.num_kv_heads, p, s, part)) return;
+    int ctx;
+    if (!find_work(item / p.num_kv_heads, p, s, part, ctx)) return;
     const int bs = p.block_size;
-    const int ctx = clamp_context(__builtin_amdgcn_readfirstlane(p.context_lens[s]), p);
     const int P = p.partition_tokens;
     const int nparts = (ctx + P - 1) / P;
     const int hq0 = kvh * G;

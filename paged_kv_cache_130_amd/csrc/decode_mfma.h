@@ -122,11 +122,11 @@ __device__ __forceinline__ void decode_mfma_wave(const DenseDecodeParams& p, int
 
     const int kvh = item % p.num_kv_heads;
     int s, part;
-    if (!find_work(item / p.num_kv_heads, p, s, part)) return;
+    int ctx;
+    if (!find_work(item / p.num_kv_heads, p, s, part, ctx)) return;
 
     const int G = p.group;
     const int bs = p.block_size;
-    const int ctx = clamp_context(__builtin_amdgcn_readfirstlane(p.context_lens[s]), p);
     const int P = p.partition_tokens;
     const int nparts = (ctx + P - 1) / P;
     const int hq0 = kvh * G;

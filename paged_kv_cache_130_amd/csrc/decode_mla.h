@@ -23,12 +23,18 @@
 //    products. (One wave per 16 heads and all 512 output dims needs about 420 registers, so only
 //    one wave fits per SIMD.)
 //  * Each 32-token unit is copied from HBM straight into LDS (lds_dma, 16 bytes per lane, four
-//    stages in flight), then dequantized once per work-group into a bf16 tile
-//    [32 rows x (512 latent * scale | 64 RoPE)]: each e4m3 value is converted exactly to fp32,
-//    multiplied by its scale and rounded to bf16. Every wave reads its score (K) and PV (V) operands
-//    from that tile; rows are swizzled so the operand reads are free of bank conflicts.
-//  * Scores S^T = K . Q^T and PV O += P . V run on v_mfma_f32_16x16x32_bf16. The score output
-//    registers are directly the PV A operand (token order sigma of mfma_common.h, two 16-token tiles
+//    stages in flight), then widened once per work-group into a bf16 tile
+//    [32 rows x (512 latent codes | 64 RoPE)]: every e4m3 code is a bf16 value, so the tile holds
+//    the codes exactly, and the unit's 4 x 32 float32 scales go to a small table beside the tile.
+//    Every wave reads its score (K) and PV (V) operands from that tile; rows are swizzled so the
+//    operand reads are free of bank conflicts.
+//  * Scores S^T = K . Q^T and PV O += P . V run on v_mfma_f32_16x16x32_bf16. The scale groups stay
+//    exact: the latent products of each 128-value group accumulate separately (4 k-steps), and
+//    each token's group sum is multiplied by its float32 scale and added in fp32; the RoPE products
+//    need no scale. On the value side the scale of token t and group g multiplies the probability:
+//    the PV A operand for output dims of group g is bf16(p_t * scale_g[t]). So the only roundings
+//    are those of fp32 accumulation and of the bf16 probabilities, as in the dense decode. The score
+//    output registers are the PV A operand's token order (sigma of mfma_common.h, two 16-token tiles
 //    per k=32 step); the V operand comes from ds_read_b64_tr_b16, which transposes 4 x 4 blocks of
 //    16-bit values across the lanes of a 16-lane group.
 //  * Per unit: one barrier; the dequantization of unit u+1 is interleaved with the products of
@@ -72,6 +78,11 @@ __shared__ __attribute__((aligned(16))) char s_raw3[kRawStage];
 __shared__ __attribute__((aligned(16))) char s_junk[1024];  // target of loads past the last window
 __shared__ __attribute__((aligned(16))) char s_tile0[kTileStage];
 __shared__ __attribute__((aligned(16))) char s_tile1[kTileStage];
+// Scales of the unit in tile stage 0 / 1: entry 32 g + 8 (r & 3) + 4 (r >> 4) + ((r >> 2) & 3) holds
+// scale g of row r, so the 8 rows a lane's score registers hold (16 t + g4 + 4 j) are 8 consecutive
+// floats. Rows without a token hold 0.
+__shared__ __attribute__((aligned(16))) float s_scale0[4 * kUnit];
+__shared__ __attribute__((aligned(16))) float s_scale1[4 * kUnit];
 // Sparse form: the slots of unit g (32 used of 64 entries) in table g % 8, copied four units ahead.
 __shared__ __attribute__((aligned(16))) int32_t s_slot[8][64];
 
@@ -86,6 +97,11 @@ template <int K>
 __device__ __forceinline__ char* tile_stage() {
     if constexpr (K == 0) return s_tile0;
     else return s_tile1;
+}
+template <int K>
+__device__ __forceinline__ float* scale_stage() {
+    if constexpr (K == 0) return s_scale0;
+    else return s_scale1;
 }
 
 // 16-byte chunk c of tile row r is stored at chunk c ^ swz(r). Tile rows are 1152 bytes, a multiple
@@ -107,12 +123,6 @@ __device__ __forceinline__ int mla_ctx(int s, const MlaDecodeParams& p) { return
 // Context of sequence s, s wave-uniform.
 __device__ __forceinline__ int mla_ctx_uniform(int s, const MlaDecodeParams& p) {
     return clamp_ctx(load_scalar(p.context_lens + s), p);
-}
-
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
 }
 
 // Position in the unit stream (all values wave-uniform).
@@ -175,16 +185,14 @@ __device__ Cursor locate(int g0, const MlaDecodeParams& p, int lane) {
     return c;
 }
 
-// Eight e4m3 bytes, times their row-quarter scale, as eight bf16 (round to nearest even). The
-// e4m3 -> fp32 conversion is exact.
-__device__ __forceinline__ uint4 dequant8(uint2 b, float sc) {
-    const f32x2_t a0 = __builtin_amdgcn_cvt_pk_f32_fp8(b.x, false);
-    const f32x2_t a1 = __builtin_amdgcn_cvt_pk_f32_fp8(b.x, true);
-    const f32x2_t a2 = __builtin_amdgcn_cvt_pk_f32_fp8(b.y, false);
-    const f32x2_t a3 = __builtin_amdgcn_cvt_pk_f32_fp8(b.y, true);
-    return make_uint4(pack2<true>(a0.x * sc, a0.y * sc), pack2<true>(a1.x * sc, a1.y * sc),
-                      pack2<true>(a2.x * sc, a2.y * sc), pack2<true>(a3.x * sc, a3.y * sc));
+// Eight e4m3 codes as eight bf16 values (exact: every e4m3 value is a bf16 value).
+__device__ __forceinline__ uint4 codes8(uint2 b) {
+    return make_uint4(e4m3x2_bf16<false>(b.x), e4m3x2_bf16<true>(b.x), e4m3x2_bf16<false>(b.y),
+                      e4m3x2_bf16<true>(b.y));
 }
+
+// Position of row r in the scale table of a unit (see s_scale0).
+__device__ __forceinline__ int scale_slot(int r) { return 8 * (r & 3) + 4 * (r >> 4) + ((r >> 2) & 3); }
 
 }  // namespace
 
@@ -380,18 +388,14 @@ void decode_mla_kernel(MlaDecodeParams p) {
     // items; conv_store converts and writes items [i0, i0 + CNT) and, if rope, the RoPE chunks.
     struct ConvIn {
         uint2 b8[kLatentIters];
-        float sc[kLatentIters];
     };
     auto conv_load = [&](auto kr, ConvIn& in) __attribute__((always_inline)) {
         constexpr int KR = decltype(kr)::value;
         const char* raw = raw_stage<KR>();
         const int conv_raw = wave * kRow + 8 * lane;
-        const int conv_scale = wave * kRow + kScaleOff + 4 * (lane >> 4);
 #pragma unroll
-        for (int it = 0; it < kLatentIters; ++it) {
+        for (int it = 0; it < kLatentIters; ++it)
             in.b8[it] = *reinterpret_cast<const uint2*>(raw + conv_raw + it * NW * kRow);
-            in.sc[it] = *reinterpret_cast<const float*>(raw + conv_scale + it * NW * kRow);
-        }
     };
     auto conv_store = [&](auto kr, auto kt, uint32_t vmask, const ConvIn& in, int i0, auto cnt, bool rope)
         __attribute__((always_inline)) {
@@ -405,7 +409,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
             const int it = i0 + jj;
             if (it < kLatentIters) {
                 const int r = it * NW + wave;  // wave-uniform
-                const uint4 d = dequant8(in.b8[it], in.sc[it]);
+                const uint4 d = codes8(in.b8[it]);
                 const bool keep = (vmask >> r) & 1u;
                 *reinterpret_cast<uint4*>(tile + r * kTileRow + ((lane ^ swz(r)) << 4)) =
                     keep ? d : make_uint4(0u, 0u, 0u, 0u);
@@ -422,6 +426,16 @@ void decode_mla_kernel(MlaDecodeParams p) {
                     *reinterpret_cast<uint4*>(tile + r * kTileRow + ((64 + (k8 ^ swz(r))) << 4)) =
                         keep ? d : make_uint4(0u, 0u, 0u, 0u);
                 }
+            }
+            // The unit's scales into the table of tile stage KT (0 for rows without a token).
+            if (tid < kUnit) {
+                const float4 sv = *reinterpret_cast<const float4*>(raw + tid * kRow + kScaleOff);
+                const bool keep = (vmask >> tid) & 1u;
+                float* st = scale_stage<KT>() + scale_slot(tid);
+                st[0] = keep ? sv.x : 0.f;
+                st[32] = keep ? sv.y : 0.f;
+                st[64] = keep ? sv.z : 0.f;
+                st[96] = keep ? sv.w : 0.f;
             }
         }
     };
@@ -506,6 +520,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
     auto compute = [&](auto kt, uint32_t vmask, auto kr2, auto kt2, uint32_t vn) __attribute__((always_inline)) {
         constexpr int KT = decltype(kt)::value;
         const char* tile = tile_stage<KT>();
+        const float* scl = scale_stage<KT>() + 8 * (lane >> 4);  // this lane's 8 rows, group 0
         const int g4 = lane >> 4;
 
         // The dequantization of the next unit starts with its LDS reads, whose results are used
@@ -513,22 +528,48 @@ void decode_mla_kernel(MlaDecodeParams p) {
         ConvIn cin;
         conv_load(kr2, cin);
 
-        // Scores: 36 A operands (t, ks), loaded kPre products ahead; two accumulator chains (t = 0, 1).
+        // Scores: 36 A operands (t, ks), loaded kPre products ahead, tiles t = 0, 1 alternating.
+        // Order: the two RoPE k-steps (16, 17) straight into S, then the latent k-steps group by
+        // group (g = 0..3: k-steps 4g .. 4g+3) into Sg, each group's sums scaled per row and added
+        // to S once its last product is issued.
         constexpr int kPre = 4;
         constexpr int kA = 2 * kKSteps;
-        f32x4_t S[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t S[2] = {zero, zero};
+        f32x4_t Sg[2] = {zero, zero};
+        auto ks_of = [](int x) constexpr { return x < 4 ? 16 + (x >> 1) : 4 * ((x - 4) >> 3) + (((x - 4) >> 1) & 3); };
         auto load_a = [&](int x) __attribute__((always_inline)) {
-            const int ks = x >> 1, t = x & 1;
+            const int ks = ks_of(x), t = x & 1;
             return *reinterpret_cast<const uint4*>(tile + ((ks & 1) ? a_odd : a_even) + t * kTile1 + (ks >> 1) * 128);
         };
         uint4 aring[kPre];
 #pragma unroll
         for (int i = 0; i < kPre; ++i) aring[i] = load_a(i);
+        float4 sg[2];  // scales of the current group for rows (t, j)
 #pragma unroll
         for (int x = 0; x < kA; ++x) {
             const uint4 a = aring[x % kPre];
             if (x + kPre < kA) aring[x % kPre] = load_a(x + kPre);
-            S[x & 1] = mfma_k32<true>(a, qr[x >> 1], S[x & 1]);
+            const int t = x & 1;
+            if (x < 4) {
+                S[t] = mfma_k32<true>(a, qr[ks_of(x)], x < 2 ? zero : S[t]);
+            } else {
+                const int y = x - 4, g = y >> 3;
+                if ((y & 7) == 0) {
+                    sg[0] = *reinterpret_cast<const float4*>(scl + 32 * g);
+                    sg[1] = *reinterpret_cast<const float4*>(scl + 32 * g + 4);
+                }
+                Sg[t] = mfma_k32<true>(a, qr[ks_of(x)], ((y >> 1) & 3) == 0 ? zero : Sg[t]);
+                if ((y & 7) == 7) {
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        S[tt][0] = fmaf(sg[tt].x, Sg[tt][0], S[tt][0]);
+                        S[tt][1] = fmaf(sg[tt].y, Sg[tt][1], S[tt][1]);
+                        S[tt][2] = fmaf(sg[tt].z, Sg[tt][2], S[tt][2]);
+                        S[tt][3] = fmaf(sg[tt].w, Sg[tt][3], S[tt][3]);
+                    }
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -581,8 +622,16 @@ void decode_mla_kernel(MlaDecodeParams p) {
         };
         if (whole_unit) unit_exp(std::false_type{});
         else unit_exp(std::true_type{});
-        const uint4 A = make_uint4(pack2<true>(pr[0][0], pr[0][1]), pack2<true>(pr[0][2], pr[0][3]),
-                                   pack2<true>(pr[1][0], pr[1][1]), pack2<true>(pr[1][2], pr[1][3]));
+        // PV A operands: p times the row's scale of each of this wave's two output groups.
+        uint4 Ag[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float* sp = scl + 32 * (2 * half + k);
+            const float4 s0 = *reinterpret_cast<const float4*>(sp);
+            const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
+            Ag[k] = make_uint4(pack2<true>(pr[0][0] * s0.x, pr[0][1] * s0.y), pack2<true>(pr[0][2] * s0.z, pr[0][3] * s0.w),
+                               pack2<true>(pr[1][0] * s1.x, pr[1][1] * s1.y), pack2<true>(pr[1][2] * s1.z, pr[1][3] * s1.w));
+        }
 
         // PV: one 16-dim output tile per product; its B operand is two transposed reads (tile rows
         // 0..15 and 16..31). The dequantization of the next unit is spread over eight groups of four.
@@ -606,7 +655,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
         for (int dt = 0; dt < kDimTiles; ++dt) {
             const uint4 bop = bring[dt % kPre];
             if (dt + kPre < kDimTiles) bring[dt % kPre] = load_b(dt + kPre);
-            O[dt] = mfma_k32<true>(A, bop, O[dt]);
+            O[dt] = mfma_k32<true>(Ag[dt / (kDimTiles / 2)], bop, O[dt]);
             if (dt % kTilesPerGroup == kTilesPerGroup - 1)
                 conv_store(kr2, kt2, vn, cin, (dt / kTilesPerGroup) * kConvPerGroup,
                            std::integral_constant<int, kConvPerGroup>{}, dt == kDimTiles - 1);

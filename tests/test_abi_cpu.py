@@ -81,11 +81,28 @@ def test_decode_status_codes():
     assert decode(mis) == E.PA_ERR_MISALIGNED
     assert decode(good_desc(), q=FAKE + 4) == E.PA_ERR_MISALIGNED
     # 4 partitions of 512 are needed for 2048 tokens: the workspace must be given.
-    need = pa.pa_decode_workspace_bytes(good_desc(), 4, 2048)
+    need = pa.pa_decode_workspace_bytes(good_desc(partition_size=512), 4, 2048)
     assert need == 4 * 8 * 4 * (2 + 128) * 4
-    assert pa.pa_decode_workspace_bytes(good_desc(), 4, 512) == 0
-    assert decode(good_desc(), max_ctx=2048) == E.PA_ERR_WORKSPACE
-    assert decode(good_desc(), max_ctx=2048, ws=FAKE, ws_bytes=need - 1) == E.PA_ERR_WORKSPACE
+    assert pa.pa_decode_workspace_bytes(good_desc(partition_size=512), 4, 512) == 0
+    assert decode(good_desc(partition_size=512), max_ctx=2048) == E.PA_ERR_WORKSPACE
+    assert decode(good_desc(partition_size=512), max_ctx=2048, ws=FAKE, ws_bytes=need - 1) == E.PA_ERR_WORKSPACE
+
+
+def test_automatic_partition_size():
+    """partition_size 0: 1024 tokens if Hkv * S * ceil(max_ctx / 1024) >= 8192, else the largest of
+    768, 512 with >= 2048 such items, else 256 (seen through the workspace size: S * Hq * parts *
+    (2 + D) floats)."""
+    def parts(num_seqs, max_ctx):
+        return pa.pa_decode_workspace_bytes(good_desc(), num_seqs, max_ctx) // (num_seqs * 8 * (2 + 128) * 4)
+    assert parts(256, 4097) == 5      # 2048 pairs x 5 partitions of 1024 >= 8192
+    assert parts(256, 1025) == 2      # 1024 x 2 = 4096 < 8192; 768: 2048 pairs x 2 >= 2048
+    assert parts(128, 1024) == 2      # 768: 1024 pairs x 2 = 2048
+    assert parts(64, 1024) == 4       # 512 pairs: 768 and 512 give 1024 items; partitions of 256
+    assert parts(4, 2048) == 8        # 32 pairs: none reaches 2048 items; partitions of 256
+    assert parts(64, 32768) == 32     # 512 pairs x 32 partitions of 1024
+    assert pa.pa_decode_workspace_bytes(good_desc(), 4, 256) == 0   # one partition: no partials
+    bs64 = good_desc(block_size=64, k_view=pa.CacheView(0, 0, 64 * 2048, 2048), v_view=pa.CacheView(0, 0, 64 * 2048, 2048))
+    assert pa.pa_decode_workspace_bytes(bs64, 4, 2048) // (4 * 8 * 130 * 4) == 8   # 256 tokens = 4 blocks
 
 
 def reshape(k=FAKE, kp=2048, v=FAKE, vp=2048, slots=FAKE, T=4, kc=FAKE, kb=64 * 16 * 2048, kview=None, vc=FAKE,

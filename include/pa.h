@@ -16,7 +16,8 @@
  *   - Ownership: every pointer argument is caller-owned memory. "Device" means
  *     memory the GPU can read (hipMalloc / torch CUDA tensors); descriptors are
  *     host memory. The library allocates nothing, keeps no state between calls
- *     and may be called from several host threads.
+ *     and may be called from several host threads. The one exception is
+ *     pa_decode_no_alloc, whose scratch is a static device array of the library.
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  *     stream). Work is enqueued asynchronously; no call synchronises or reads
  *     device memory on the host.
@@ -45,7 +46,10 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
+
+/* Size of the static device scratch array behind pa_decode_no_alloc (bytes, per GPU). */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum pa_status {
     PA_OK = 0,
@@ -55,7 +59,9 @@ typedef enum pa_status {
     PA_ERR_MISALIGNED = 4,        /* a pointer, stride or row width breaks the stated alignment */
     PA_ERR_VIEW_OUT_OF_RANGE = 5, /* a cache view's rows reach past the stated allocation size */
     PA_ERR_WORKSPACE = 6,         /* workspace NULL or smaller than the *_workspace_bytes query */
-    PA_ERR_HIP = 7                /* a HIP launch failed; see pa_last_hip_error() */
+    PA_ERR_HIP = 7,               /* a HIP launch failed; see pa_last_hip_error() */
+    PA_ERR_SCRATCH_LIMIT = 8      /* pa_decode_no_alloc: the call needs more than
+                                     PA_STATIC_SCRATCH_BYTES of scratch */
 } pa_status;
 
 /* KV storage formats.
@@ -261,6 +267,28 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
                   const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
                   int32_t num_seqs, int32_t max_context_len, float scale, const pa_attn_desc* desc,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_decode_no_alloc: pa_decode without a workspace argument and without any allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Computes exactly what pa_decode computes, with the same
+ * kernels and bitwise the same results. The split-context partials go to a static device array of
+ * PA_STATIC_SCRATCH_BYTES (64 MiB) that every GPU the library runs on holds until the process ends.
+ * Its address is looked up once per device, on the first call that needs it. The call calls no
+ * allocator (no hipMalloc, no hipFree).
+ *
+ *   Arguments as for pa_decode, without workspace and workspace_bytes.
+ *   Returns PA_ERR_SCRATCH_LIMIT, enqueueing nothing, when
+ *   pa_decode_workspace_bytes(desc, num_seqs, max_context_len) > PA_STATIC_SCRATCH_BYTES.
+ *   Every other error is pa_decode's.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on one GPU (on different
+ * streams, or from several host threads without ordering) race and give undefined results. Calls
+ * ordered on one stream are safe. The array keeps the last call's contents; nothing in it needs to
+ * start at zero, because each call writes every partial it reads. */
+int32_t pa_decode_no_alloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t max_context_len, float scale, const pa_attn_desc* desc,
+                           void* stream);
 
 /* Workspace bytes pa_prefill_chunk needs. */
 size_t pa_prefill_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t total_q,

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     dense_view,
     pa_copy_blocks,
     pa_decode,
+    pa_decode_no_alloc,
     pa_decode_workspace_bytes,
     pa_indexer_topk,
     pa_mla_sparse_decode,

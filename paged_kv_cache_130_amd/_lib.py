@@ -23,6 +23,9 @@ PA_ERR_MISALIGNED = 4
 PA_ERR_VIEW_OUT_OF_RANGE = 5
 PA_ERR_WORKSPACE = 6
 PA_ERR_HIP = 7
+PA_ERR_SCRATCH_LIMIT = 8
+
+PA_STATIC_SCRATCH_BYTES = 64 << 20  # pa_decode_no_alloc's static scratch per GPU
 
 PA_KV_F16 = 0
 PA_KV_BF16 = 1
@@ -32,7 +35,7 @@ PA_KV_FP8_E4M3 = 3
 EXPORTS = ("pa_abi_version", "pa_status_string", "pa_last_hip_error", "pa_reshape_and_cache", "pa_quantize_and_cache_mla",
            "pa_copy_blocks", "pa_quantize_and_cache",
            "pa_decode_workspace_bytes", "pa_decode", "pa_prefill_workspace_bytes", "pa_prefill_chunk",
-           "pa_indexer_topk", "pa_mla_sparse_decode")
+           "pa_indexer_topk", "pa_mla_sparse_decode", "pa_decode_no_alloc")
 
 
 class pa_cache_view(ctypes.Structure):
@@ -81,6 +84,8 @@ def _load():
         "pa_decode_workspace_bytes": (SZ, [ctypes.POINTER(pa_attn_desc), I32, I32]),
         "pa_decode": (I32, [P, P, P, P, P, I32, P, I32, I32, ctypes.c_float, ctypes.POINTER(pa_attn_desc), P, SZ,
                             P]),
+        "pa_decode_no_alloc": (I32, [P, P, P, P, P, I32, P, I32, I32, ctypes.c_float, ctypes.POINTER(pa_attn_desc),
+                                     P]),
         "pa_prefill_workspace_bytes": (SZ, [ctypes.POINTER(pa_attn_desc), I32, I32, I32, I32]),
         "pa_prefill_chunk": (I32, [P, P, P, P, P, I32, P, P, I32, I32, I32, I32, ctypes.c_float,
                                    ctypes.POINTER(pa_attn_desc), P, SZ, P]),
@@ -298,6 +303,19 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
                         block_tables.shape[1], _ptr(context_lens), B, int(max_context_len), float(scale),
                         ctypes.byref(d), _ptr(workspace), ws_bytes, _stream(stream))
     _check("pa_decode", st)
+
+
+def pa_decode_no_alloc(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int, scale: float,
+                       desc: AttnDesc, stream=None):
+    _require_device(out, q, k_cache, v_cache, block_tables, context_lens)
+    for name, t in (("out", out), ("q", q), ("block_tables", block_tables), ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    d = desc.c()
+    st = _lib.pa_decode_no_alloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                 block_tables.shape[1], _ptr(context_lens), context_lens.numel(),
+                                 int(max_context_len), float(scale), ctypes.byref(d), _stream(stream))
+    _check("pa_decode_no_alloc", st)
 
 
 def pa_prefill_workspace_bytes(desc: AttnDesc, num_seqs: int, total_q: int, max_query_len: int,

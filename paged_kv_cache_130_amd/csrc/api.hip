@@ -5,9 +5,15 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/pa.h"
 #include "pa_internal.h"
+
+// Scratch of pa_decode_no_alloc: the split-context partials of its kernels, one copy per GPU,
+// held until the process ends. Host code must not use this name as a device address (it names a
+// host-side stand-in); it uses the per-device address from hipGetSymbolAddress below.
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -180,17 +186,72 @@ size_t mla_decode_ws(const MlaLayout& L, int32_t num_q_heads, int32_t num_seqs) 
     return (size_t)L.slots * num_q_heads * (512 + 2) * sizeof(float) + (size_t)num_seqs * 2 * sizeof(int32_t);
 }
 
+// Device address of `scratch` on the device that runs `stream`, resolved once per device (with that
+// device current) and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+int32_t static_scratch(void* stream, void** addr) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    int dev = cur;
+    if (stream != nullptr) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd);
+        if (e != hipSuccess) return hip_status(e);
+        dev = (int)sd;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (dev != cur) {
+                const hipError_t e2 = hipSetDevice(cur);
+                if (e == hipSuccess) e = e2;
+            }
+            if (e != hipSuccess || p == nullptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *addr = p;
+    return PA_OK;
+}
+
+// The workspace of a decode call: the caller's (checked against `need`), or, for
+// pa_decode_no_alloc, the static scratch of the stream's device (need <= PA_STATIC_SCRATCH_BYTES).
+// Runs after every other argument check, so a rejected call never touches the device.
+int32_t take_workspace(size_t need, bool no_alloc, void* stream, void*& workspace, size_t& workspace_bytes) {
+    if (no_alloc) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need == 0) return PA_OK;
+        if (need > PA_STATIC_SCRATCH_BYTES) return PA_ERR_SCRATCH_LIMIT;
+        workspace_bytes = PA_STATIC_SCRATCH_BYTES;
+        return static_scratch(stream, &workspace);
+    }
+    if (need == 0) return PA_OK;
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PA_ERR_MISALIGNED;
+    return PA_OK;
+}
+
 // The MLA decode, dense (through block_tables) or sparse (through slots); the descriptor and the
 // common pointers are already checked.
 int32_t mla_decode_call(void* out, const void* q, const void* k_cache, const int32_t* block_tables,
                         int32_t bt_stride, const int32_t* slots, int64_t slot_stride, const int32_t* lens,
                         int32_t num_seqs, int32_t max_len, float scale, const pa_attn_desc& d, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, bool no_alloc, void* stream) {
     MlaLayout L;
     if (!mla_layout(d, num_seqs, max_len, L)) return PA_ERR_UNSUPPORTED;
     const size_t need = mla_decode_ws(L, d.num_q_heads, num_seqs);
-    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return PA_ERR_MISALIGNED;
+    const int32_t st = take_workspace(need, no_alloc, stream, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
     pa::MlaDecodeParams p;
     std::memset(&p, 0, sizeof(p));
     p.out = out;
@@ -244,6 +305,7 @@ const char* pa_status_string(int32_t s) {
         case PA_ERR_VIEW_OUT_OF_RANGE: return "cache view reaches past the allocation";
         case PA_ERR_WORKSPACE: return "workspace missing or too small";
         case PA_ERR_HIP: return "HIP launch failed";
+        case PA_ERR_SCRATCH_LIMIT: return "call needs more than the library's static scratch";
         default: return "unknown status";
     }
 }
@@ -433,9 +495,16 @@ size_t pa_decode_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int
     return 0;
 }
 
-int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                  int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
-                  float scale, const pa_attn_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode and pa_decode_no_alloc: every argument check, then the workspace (the caller's or the
+// static scratch), then the launches.
+int32_t decode_entry(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t max_context_len, float scale, const pa_attn_desc* desc, void* workspace,
+                     size_t workspace_bytes, bool no_alloc, void* stream) {
     if (!desc) return PA_ERR_NULL_POINTER;
     if (num_seqs < 0 || max_context_len < 0) return PA_ERR_INVALID_ARGUMENT;
     if (num_seqs == 0) return PA_OK;
@@ -451,14 +520,14 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
         return PA_ERR_MISALIGNED;
     if (mla)
         return mla_decode_call(out, q, k_cache, block_tables, bt_stride, nullptr, 0, context_lens, num_seqs,
-                               max_context_len, scale, d, workspace, workspace_bytes, stream);
+                               max_context_len, scale, d, workspace, workspace_bytes, no_alloc, stream);
     const int32_t P = effective_partition(d, num_seqs, max_context_len);
     const int64_t max_parts64 = ((int64_t)max_context_len + P - 1) / P;
     const int32_t max_parts = max_parts64 < 1 ? 1 : (int32_t)max_parts64;
-    const size_t need = dense_decode_ws(d, num_seqs, max_context_len);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-    if (need > 0 && !aligned(workspace, 16)) return PA_ERR_MISALIGNED;
     if ((int64_t)d.num_kv_heads * num_seqs * max_parts > 0x7FFFFFFFLL - 64) return PA_ERR_UNSUPPORTED;
+    const size_t need = dense_decode_ws(d, num_seqs, max_context_len);
+    st = take_workspace(need, no_alloc, stream, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
 
     pa::DenseDecodeParams p;
     std::memset(&p, 0, sizeof(p));
@@ -495,6 +564,25 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
     return hip_status(pa::launch_decode_dense(p, static_cast<hipStream_t>(stream)));
 }
 
+}  // namespace
+
+extern "C" {
+
+int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                  int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                  float scale, const pa_attn_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_entry(out, q, k_cache, v_cache, block_tables, bt_stride, context_lens, num_seqs, max_context_len,
+                        scale, desc, workspace, workspace_bytes, false, stream);
+}
+
+int32_t pa_decode_no_alloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t max_context_len, float scale, const pa_attn_desc* desc,
+                           void* stream) {
+    return decode_entry(out, q, k_cache, v_cache, block_tables, bt_stride, context_lens, num_seqs, max_context_len,
+                        scale, desc, nullptr, 0, true, stream);
+}
+
 size_t pa_prefill_workspace_bytes(const pa_attn_desc* desc, int32_t num_seqs, int32_t total_q,
                                   int32_t max_query_len, int32_t max_seq_len) {
     (void)total_q;
@@ -526,8 +614,8 @@ int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const vo
         !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4))
         return PA_ERR_MISALIGNED;
     const size_t need = dense_decode_ws(d, num_seqs, max_seq_len);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-    if (need > 0 && !aligned(workspace, 16)) return PA_ERR_MISALIGNED;
+    st = take_workspace(need, false, stream, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
     const int32_t P = effective_partition(d, num_seqs, max_seq_len);
     const int64_t max_parts64 = ((int64_t)max_seq_len + P - 1) / P;
     const int32_t max_parts = max_parts64 < 1 ? 1 : (int32_t)max_parts64;
@@ -622,7 +710,7 @@ int32_t pa_mla_sparse_decode(void* out, const void* q, const void* kv_cache, con
         !aligned(slot_counts, 4))
         return PA_ERR_MISALIGNED;
     return mla_decode_call(out, q, kv_cache, nullptr, 0, slots, slot_stride, slot_counts, num_seqs,
-                           std::min(max_count, slot_stride), scale, d, workspace, workspace_bytes, stream);
+                           std::min(max_count, slot_stride), scale, d, workspace, workspace_bytes, false, stream);
 }
 
 int32_t pa_indexer_topk(int32_t* topk_positions, int32_t* topk_slots, int32_t* topk_lens, int32_t top_k, float* scores,

@@ -26,11 +26,11 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
-    assert pa.abi_version() == 3
+    assert pa.abi_version() == 4
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         assert pa.status_string(code) and pa.status_string(code) != "unknown status"
     assert pa.status_string(99) == "unknown status"
 
@@ -103,6 +103,27 @@ def test_automatic_partition_size():
     assert pa.pa_decode_workspace_bytes(good_desc(), 4, 256) == 0   # one partition: no partials
     bs64 = good_desc(block_size=64, k_view=pa.CacheView(0, 0, 64 * 2048, 2048), v_view=pa.CacheView(0, 0, 64 * 2048, 2048))
     assert pa.pa_decode_workspace_bytes(bs64, 4, 2048) // (4 * 8 * 130 * 4) == 8   # 256 tokens = 4 blocks
+
+
+def decode_no_alloc(desc, num_seqs=4, max_ctx=300, q=FAKE):
+    d = desc.c() if desc is not None else None
+    return L._lib.pa_decode_no_alloc(FAKE, q, FAKE, FAKE, FAKE, 256, FAKE, num_seqs, max_ctx, 0.1,
+                                     ctypes.byref(d) if d is not None else None, None)
+
+
+def test_decode_no_alloc_status_codes():
+    E = L
+    assert decode_no_alloc(None) == E.PA_ERR_NULL_POINTER
+    assert decode_no_alloc(good_desc(), num_seqs=-1) == E.PA_ERR_INVALID_ARGUMENT
+    assert decode_no_alloc(good_desc(), num_seqs=0) == E.PA_OK
+    # 4096 sequences x 8 heads x 5 partitions of (2 + 128) floats: 85 MB of partials > 64 MiB.
+    assert pa.pa_decode_workspace_bytes(good_desc(partition_size=512), 4096, 2560) > L.PA_STATIC_SCRATCH_BYTES
+    assert decode_no_alloc(good_desc(partition_size=512), num_seqs=4096, max_ctx=2560) == E.PA_ERR_SCRATCH_LIMIT
+    # Bad descriptors and pointers fail as in pa_decode, before any device call.
+    assert decode_no_alloc(good_desc(block_size=24)) == E.PA_ERR_UNSUPPORTED
+    assert decode_no_alloc(good_desc(partition_size=40)) == E.PA_ERR_INVALID_ARGUMENT
+    assert decode_no_alloc(good_desc(), q=None) == E.PA_ERR_NULL_POINTER
+    assert decode_no_alloc(good_desc(), q=FAKE + 4) == E.PA_ERR_MISALIGNED
 
 
 def reshape(k=FAKE, kp=2048, v=FAKE, vp=2048, slots=FAKE, T=4, kc=FAKE, kb=64 * 16 * 2048, kview=None, vc=FAKE,

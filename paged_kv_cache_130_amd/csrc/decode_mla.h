@@ -17,17 +17,20 @@
 //    waves owns 16 heads and one half (256 dims) of their outputs: two waves per 16 heads, up to
 //    eight waves, two per SIMD. A wave holds its heads' queries (18 k-steps, 72 registers) and its
 //    outputs (16 heads x 256 fp32, 64 registers) for a whole segment, so the only operands streamed
-//    are K and V. The two waves of a head group both compute the group's scores and softmax (the
-//    same values): 52 products a wave per unit instead of 34, but no exchange through LDS;
-//    with a second wave per SIMD one wave's softmax and dequantization run beside the other's
-//    products. (One wave per 16 heads and all 512 output dims needs about 420 registers, so only
-//    one wave fits per SIMD.)
-//  * Each 32-token unit is copied from HBM straight into LDS (lds_dma, 16 bytes per lane, four
-//    stages in flight), then widened once per work-group into a bf16 tile
+//    are K and V. The two waves of a head group split the scores: each computes its own 16-token
+//    tile of the unit (18 products) and its probabilities against its own reference, and they trade
+//    probabilities and references through LDS (one barrier). Both then take the larger reference
+//    and rescale both tiles' probabilities with the same fp32 operations, so they hold bitwise the
+//    same 32 probabilities; each runs PV for its 256 dims (16 products). So a wave issues 34 products
+//    per unit, the algorithmic count.
+//  * Each 32-token unit is copied from HBM straight into LDS (lds_dma, 16 bytes per lane; three raw
+//    stages, three units in flight), then widened once per work-group into a bf16 tile
 //    [32 rows x (512 latent codes | 64 RoPE)]: every e4m3 code is a bf16 value, so the tile holds
 //    the codes exactly, and the unit's 4 x 32 float32 scales go to a small table beside the tile.
-//    Every wave reads its score (K) and PV (V) operands from that tile; rows are swizzled so the
-//    operand reads are free of bank conflicts.
+//    Every read of a raw stage happens at the start of a step, so the stage takes the next unit's
+//    copy right after the score exchange, in the middle of the step. Every wave reads its score (K)
+//    and PV (V) operands from the tile; rows are swizzled so the operand reads are free of bank
+//    conflicts.
 //  * Scores S^T = K . Q^T and PV O += P . V run on v_mfma_f32_16x16x32_bf16. The scale groups stay
 //    exact: the latent products of each 128-value group accumulate separately (4 k-steps), and
 //    each token's group sum is multiplied by its float32 scale and added in fp32; the RoPE products
@@ -37,10 +40,10 @@
 //    output registers are the PV A operand's token order (sigma of mfma_common.h, two 16-token tiles
 //    per k=32 step); the V operand comes from ds_read_b64_tr_b16, which transposes 4 x 4 blocks of
 //    16-bit values across the lanes of a 16-lane group.
-//  * Per unit: one barrier; the dequantization of unit u+1 is interleaved with the products of
-//    unit u, and operands are loaded four products ahead. The softmax is online (lazy reference, as
-//    in the dense decode) and a segment that is not a whole sequence writes an fp32 partial merged
-//    by mla_merge_kernel (log-sum-exp).
+//  * Per unit: the opening barrier and the exchange barrier; the widening of unit u+1 is
+//    interleaved with the PV products of unit u, and operands are loaded four products ahead. The
+//    softmax is online (lazy reference, as in the dense decode) and a segment that is not a whole
+//    sequence writes an fp32 partial merged by mla_merge_kernel (log-sum-exp).
 
 #pragma once
 
@@ -68,13 +71,12 @@ constexpr int kLatentChunks = kUnit * 64;          // 16-byte bf16 chunks of deq
 constexpr int kRopeChunks = kUnit * 8;
 constexpr int kKSteps = 18;                        // k=32 steps over 576 score dims
 
-// Raw rows arrive in four stages and the dequantized tile has two. They are separate objects rather
+// Raw rows arrive in three stages and the widened tile has two. They are separate objects rather
 // than one indexed array so that the compiler can tell the stage being read from those still being
 // filled by the direct-to-LDS loads, and does not wait for all of them.
 __shared__ __attribute__((aligned(16))) char s_raw0[kRawStage];
 __shared__ __attribute__((aligned(16))) char s_raw1[kRawStage];
 __shared__ __attribute__((aligned(16))) char s_raw2[kRawStage];
-__shared__ __attribute__((aligned(16))) char s_raw3[kRawStage];
 __shared__ __attribute__((aligned(16))) char s_junk[1024];  // target of loads past the last window
 __shared__ __attribute__((aligned(16))) char s_tile0[kTileStage];
 __shared__ __attribute__((aligned(16))) char s_tile1[kTileStage];
@@ -83,15 +85,18 @@ __shared__ __attribute__((aligned(16))) char s_tile1[kTileStage];
 // floats. Rows without a token hold 0.
 __shared__ __attribute__((aligned(16))) float s_scale0[4 * kUnit];
 __shared__ __attribute__((aligned(16))) float s_scale1[4 * kUnit];
-// Sparse form: the slots of unit g (32 used of 64 entries) in table g % 8, copied four units ahead.
+// Sparse form: the slots of unit g (32 used of 64 entries) in table g % 8, copied three units ahead.
 __shared__ __attribute__((aligned(16))) int32_t s_slot[8][64];
+// Score exchange between the two waves that own the same 16 heads: per wave, the probabilities of
+// its 16-token tile for its 16 heads (against its own reference) and that reference per head.
+__shared__ __attribute__((aligned(16))) float s_xp[8][16 * 16];
+__shared__ __attribute__((aligned(16))) float s_xm[8][16];
 
 template <int K>
 __device__ __forceinline__ char* raw_stage() {
     if constexpr (K == 0) return s_raw0;
     else if constexpr (K == 1) return s_raw1;
-    else if constexpr (K == 2) return s_raw2;
-    else return s_raw3;
+    else return s_raw2;
 }
 template <int K>
 __device__ __forceinline__ char* tile_stage() {
@@ -263,8 +268,9 @@ void decode_mla_kernel(MlaDecodeParams p) {
     f32x4_t O[kDimTiles];  // register j of lane (c, g4): head 4 g4 + j, dim 16 (dt0 + dt) + c
     const int dt0 = half * kDimTiles;
     float m = kNegInf, l = 0.f;
-    // Unit validity, one mask per raw stage: bit r set when row r holds a token of the unit.
-    uint32_t info[4];
+    // Unit validity, bit r set when row r holds a token of the unit; the mask of unit u is kept in
+    // info[u % 6] from its copy (step u - 4) to its compute (step u).
+    uint32_t info[6];
 
     Cursor cc = locate(g_begin, p, lane);  // unit being computed
     Cursor cl = cc;                        // next unit to load
@@ -306,13 +312,14 @@ void decode_mla_kernel(MlaDecodeParams p) {
         advance(cs, p);
     };
 
-    auto issue_sparse = [&](auto kst) __attribute__((always_inline)) {
+    auto issue_sparse = [&](auto kst, auto kinf) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
+        constexpr int KI = decltype(kinf)::value;
         const int v = cl.g < g_end ? min(kUnit, cl.ctx - cl.k * kUnit) : 0;
         const int32_t* tab = s_slot[cl.g & 7];
         const uint32_t nslots = (uint32_t)p.num_slots;
         const int32_t mine = tab[lane & 31];
-        info[K] = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && lane < v && (uint32_t)mine < nslots);
+        info[KI] = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && lane < v && (uint32_t)mine < nslots);
         char* stage = raw_stage<K>();
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -330,10 +337,11 @@ void decode_mla_kernel(MlaDecodeParams p) {
         advance(cl, p);
     };
 
-    auto issue = [&](auto kst) __attribute__((always_inline)) {
+    auto issue = [&](auto kst, auto kinf) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
+        constexpr int KI = decltype(kinf)::value;
         if constexpr (SPARSE) {
-            issue_sparse(kst);
+            issue_sparse(kst, kinf);
             return;
         }
         const bool live = cl.g < g_end;
@@ -368,7 +376,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
                 }
             }
         }
-        info[K] = (v >= 32 ? 0xFFFFFFFFu : (1u << v) - 1u) & ((ok_a ? 0xFFFFu : 0u) | (ok_b ? 0xFFFF0000u : 0u));
+        info[KI] = (v >= 32 ? 0xFFFFFFFFu : (1u << v) - 1u) & ((ok_a ? 0xFFFFu : 0u) | (ok_b ? 0xFFFF0000u : 0u));
         char* stage = raw_stage<K>();
         const bool split = p.block_size < kUnit;
 #pragma unroll
@@ -388,7 +396,11 @@ void decode_mla_kernel(MlaDecodeParams p) {
     // items; conv_store converts and writes items [i0, i0 + CNT) and, if rope, the RoPE chunks.
     struct ConvIn {
         uint2 b8[kLatentIters];
+        uint4 rope[kRopeIters];
+        float4 scl;
     };
+    // Every read of the raw stage happens here, so that the stage is free for the next copy once
+    // these reads are done.
     auto conv_load = [&](auto kr, ConvIn& in) __attribute__((always_inline)) {
         constexpr int KR = decltype(kr)::value;
         const char* raw = raw_stage<KR>();
@@ -396,13 +408,18 @@ void decode_mla_kernel(MlaDecodeParams p) {
 #pragma unroll
         for (int it = 0; it < kLatentIters; ++it)
             in.b8[it] = *reinterpret_cast<const uint2*>(raw + conv_raw + it * NW * kRow);
+#pragma unroll
+        for (int it = 0; it < kRopeIters; ++it) {
+            const int n = it * 64 * NW + tid;
+            if (kRopeChunks % (64 * NW) == 0 || n < kRopeChunks)
+                in.rope[it] = *reinterpret_cast<const uint4*>(raw + (n >> 3) * kRow + kRopeOff + 16 * (n & 7));
+        }
+        if (tid < kUnit) in.scl = *reinterpret_cast<const float4*>(raw + tid * kRow + kScaleOff);
     };
     auto conv_store = [&](auto kr, auto kt, uint32_t vmask, const ConvIn& in, int i0, auto cnt, bool rope)
         __attribute__((always_inline)) {
-        constexpr int KR = decltype(kr)::value;
         constexpr int KT = decltype(kt)::value;
         constexpr int CNT = decltype(cnt)::value;
-        const char* raw = raw_stage<KR>();
         char* tile = tile_stage<KT>();
 #pragma unroll
         for (int jj = 0; jj < CNT; ++jj) {
@@ -421,7 +438,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
                 const int n = it * 64 * NW + tid;
                 if (kRopeChunks % (64 * NW) == 0 || n < kRopeChunks) {
                     const int r = n >> 3, k8 = n & 7;
-                    const uint4 d = *reinterpret_cast<const uint4*>(raw + r * kRow + kRopeOff + 16 * k8);
+                    const uint4 d = in.rope[it];
                     const bool keep = (vmask >> r) & 1u;
                     *reinterpret_cast<uint4*>(tile + r * kTileRow + ((64 + (k8 ^ swz(r))) << 4)) =
                         keep ? d : make_uint4(0u, 0u, 0u, 0u);
@@ -429,7 +446,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
             }
             // The unit's scales into the table of tile stage KT (0 for rows without a token).
             if (tid < kUnit) {
-                const float4 sv = *reinterpret_cast<const float4*>(raw + tid * kRow + kScaleOff);
+                const float4 sv = in.scl;
                 const bool keep = (vmask >> tid) & 1u;
                 float* st = scale_stage<KT>() + scale_slot(tid);
                 st[0] = keep ? sv.x : 0.f;
@@ -517,7 +534,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
     // PV slots. Each slot loads the next slot's LDS operands, then issues its own products; the
     // scheduling barriers keep the compiler from hoisting every operand load to the top, which would
     // need more registers than the queries and outputs leave free.
-    auto compute = [&](auto kt, uint32_t vmask, auto kr2, auto kt2, uint32_t vn) __attribute__((always_inline)) {
+    auto compute = [&](auto kt, uint32_t vmask, auto kr2, auto kt2, uint32_t vn, auto ki4) __attribute__((always_inline)) {
         constexpr int KT = decltype(kt)::value;
         const char* tile = tile_stage<KT>();
         const float* scl = scale_stage<KT>() + 8 * (lane >> 4);  // this lane's 8 rows, group 0
@@ -528,77 +545,93 @@ void decode_mla_kernel(MlaDecodeParams p) {
         ConvIn cin;
         conv_load(kr2, cin);
 
-        // Scores: 36 A operands (t, ks), loaded kPre products ahead, tiles t = 0, 1 alternating.
-        // Order: the two RoPE k-steps (16, 17) straight into S, then the latent k-steps group by
-        // group (g = 0..3: k-steps 4g .. 4g+3) into Sg, each group's sums scaled per row and added
-        // to S once its last product is issued.
+        // Scores of this wave's own 16-token tile (t = half): 18 A operands, loaded kPre products
+        // ahead. Order: the two RoPE k-steps (16, 17) into S, then the latent k-steps group by group
+        // (g = 0..3: k-steps 4g .. 4g+3) into Sg[0] / Sg[1] (two accumulator chains, even and odd
+        // k-steps); once a group's last product is issued, its sums are scaled per row and added to
+        // S. Register j holds token 16 half + g4 + 4j of head column c.
         constexpr int kPre = 4;
-        constexpr int kA = 2 * kKSteps;
+        constexpr int kA = kKSteps;
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t S[2] = {zero, zero};
+        f32x4_t S = zero;
         f32x4_t Sg[2] = {zero, zero};
-        auto ks_of = [](int x) constexpr { return x < 4 ? 16 + (x >> 1) : 4 * ((x - 4) >> 3) + (((x - 4) >> 1) & 3); };
+        auto ks_of = [](int x) constexpr { return x < 2 ? 16 + x : x - 2; };
+        const char* atile = tile + half * kTile1;
         auto load_a = [&](int x) __attribute__((always_inline)) {
-            const int ks = ks_of(x), t = x & 1;
-            return *reinterpret_cast<const uint4*>(tile + ((ks & 1) ? a_odd : a_even) + t * kTile1 + (ks >> 1) * 128);
+            const int ks = ks_of(x);
+            return *reinterpret_cast<const uint4*>(atile + ((ks & 1) ? a_odd : a_even) + (ks >> 1) * 128);
         };
         uint4 aring[kPre];
 #pragma unroll
         for (int i = 0; i < kPre; ++i) aring[i] = load_a(i);
-        float4 sg[2];  // scales of the current group for rows (t, j)
+        float4 sg;  // scales of the current group for this lane's rows j
 #pragma unroll
         for (int x = 0; x < kA; ++x) {
             const uint4 a = aring[x % kPre];
             if (x + kPre < kA) aring[x % kPre] = load_a(x + kPre);
-            const int t = x & 1;
-            if (x < 4) {
-                S[t] = mfma_k32<true>(a, qr[ks_of(x)], x < 2 ? zero : S[t]);
+            if (x < 2) {
+                S = mfma_k32<true>(a, qr[ks_of(x)], x == 0 ? zero : S);
             } else {
-                const int y = x - 4, g = y >> 3;
-                if ((y & 7) == 0) {
-                    sg[0] = *reinterpret_cast<const float4*>(scl + 32 * g);
-                    sg[1] = *reinterpret_cast<const float4*>(scl + 32 * g + 4);
-                }
-                Sg[t] = mfma_k32<true>(a, qr[ks_of(x)], ((y >> 1) & 3) == 0 ? zero : Sg[t]);
-                if ((y & 7) == 7) {
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        S[tt][0] = fmaf(sg[tt].x, Sg[tt][0], S[tt][0]);
-                        S[tt][1] = fmaf(sg[tt].y, Sg[tt][1], S[tt][1]);
-                        S[tt][2] = fmaf(sg[tt].z, Sg[tt][2], S[tt][2]);
-                        S[tt][3] = fmaf(sg[tt].w, Sg[tt][3], S[tt][3]);
-                    }
+                const int y = x - 2, g = y >> 2, kk = y & 3;
+                if (kk == 0) sg = *reinterpret_cast<const float4*>(scl + 32 * g + 4 * half);
+                Sg[kk & 1] = mfma_k32<true>(a, qr[ks_of(x)], kk < 2 ? zero : Sg[kk & 1]);
+                if (kk == 3) {
+                    S[0] = fmaf(sg.x, Sg[0][0] + Sg[1][0], S[0]);
+                    S[1] = fmaf(sg.y, Sg[0][1] + Sg[1][1], S[1]);
+                    S[2] = fmaf(sg.z, Sg[0][2] + Sg[1][2], S[2]);
+                    S[3] = fmaf(sg.w, Sg[0][3] + Sg[1][3], S[3]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // Register j of tile t holds token 16t + g4 + 4j of head column c. Rows past the unit's valid
-        // ones (in the last unit of a sequence, or in an invalid block) are masked out; a whole unit,
-        // the usual case, takes the branch without the masks (vmask is wave-uniform).
-        const bool whole_unit = vmask == 0xFFFFFFFFu;
-        auto row_ok = [&](auto masked, int t, int j) __attribute__((always_inline)) -> bool {
-            if constexpr (decltype(masked)::value) return (vmask >> (16 * t + g4 + 4 * j)) & 1u;
-            else return true;
-        };
-        auto unit_max = [&](auto masked) __attribute__((always_inline)) {
-            float mx = kNegInf;
+        // Rows past the unit's valid ones (in the last unit of a sequence, or in an invalid block or
+        // slot) are masked out.
+        bool ok[4];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+        for (int jj = 0; jj < 4; ++jj) ok[jj] = (vmask >> (16 * half + g4 + 4 * jj)) & 1u;
+        float mx = kNegInf;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mx = row_ok(masked, t, j) ? fmaxf(mx, S[t][j]) : mx;
-            return mx;
-        };
-        float mx = whole_unit ? unit_max(std::false_type{}) : unit_max(std::true_type{});
+        for (int jj = 0; jj < 4; ++jj) mx = ok[jj] ? fmaxf(mx, S[jj]) : mx;
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // This tile's probabilities against the wave's own reference: the running reference m, moved
+        // to the tile maximum if that exceeds it by more than kRescaleSlack (so p <= 2^kRescaleSlack).
         const float tmax = mx * sl2;
-        const bool need = tmax > m + kRescaleSlack;
+        const float m_own = tmax > m + kRescaleSlack ? tmax : m;
+        float po[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const float ex = fast_exp2(fmaf(S[jj], sl2, -m_own));
+            po[jj] = ok[jj] ? ex : 0.f;
+        }
+        // Exchange with the wave that owns the same heads and the other tile: probabilities (token
+        // g4 + 4j of the tile, head c at float (g4 + 4j) * 16 + c) and the reference per head.
+        float* xo = s_xp[wave];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) xo[(g4 + 4 * jj) * 16 + (lane & 15)] = po[jj];
+        if (g4 == 0) s_xm[wave][lane] = m_own;
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));  // own LDS writes done (copies may stay in flight)
+        lds_barrier();
+        // Every wave has read the raw stage of the unit it is dequantizing (conv_load, waited for
+        // above): the next unit's copy can go there now, in the middle of the step, rather than with
+        // every other wave's right after the step's opening barrier.
+        issue(kr2, ki4);
+        const int partner = wave < kHeadWaves ? wave + kHeadWaves : wave - kHeadWaves;
+        const float* xq = s_xp[partner];
+        float pq[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) pq[jj] = xq[(g4 + 4 * jj) * 16 + (lane & 15)];
+        const float m_par = s_xm[partner][lane & 15];
+        // Common reference: the larger of the two (both waves compute the same value, and from it
+        // the same factors and probabilities, bit for bit).
+        const float m_new = fmaxf(m_own, m_par);
+        const float f_own = m_own == m_new ? 1.f : fast_exp2(m_own - m_new);
+        const float f_par = m_par == m_new ? 1.f : fast_exp2(m_par - m_new);
+        const bool need = m_new > m;
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-            const float mnew = need ? tmax : m;
-            const float alpha = need ? fast_exp2(m - mnew) : 1.f;
+            const float alpha = need ? fast_exp2(m - m_new) : 1.f;
             l *= alpha;
-            m = mnew;
             const f32x4_t av = {__shfl(alpha, 4 * g4), __shfl(alpha, 4 * g4 + 1), __shfl(alpha, 4 * g4 + 2),
                                 __shfl(alpha, 4 * g4 + 3)};
             // One output tile at a time: the scheduling barriers keep the compiler from reading every
@@ -609,19 +642,19 @@ void decode_mla_kernel(MlaDecodeParams p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        m = m_new;
+        // Tile 0 and tile 1 probabilities against m, summed into l in that order by both waves.
         float pr[2][4];
-        auto unit_exp = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+        for (int jj = 0; jj < 4; ++jj) {
+            const float a0 = po[jj] * f_own, a1 = pq[jj] * f_par;
+            pr[0][jj] = half == 0 ? a0 : a1;
+            pr[1][jj] = half == 0 ? a1 : a0;
+        }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float ex = fast_exp2(fmaf(S[t][j], sl2, -m));
-                    pr[t][j] = row_ok(masked, t, j) ? ex : 0.f;
-                    l += pr[t][j];
-                }
-        };
-        if (whole_unit) unit_exp(std::false_type{});
-        else unit_exp(std::true_type{});
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) l += pr[t][jj];
         // PV A operands: p times the row's scale of each of this wave's two output groups.
         uint4 Ag[2];
 #pragma unroll
@@ -663,44 +696,43 @@ void decode_mla_kernel(MlaDecodeParams p) {
         }
     };
 
-    // Step of unit u (K = u % 4): wait for unit u+1's rows, start loading unit u+4, compute unit u
-    // while dequantizing unit u+1. Returns false when the range is done.
+    // Step of unit u (K = u % 6; raw stage u % 3, tile stage u % 2): wait for unit u+1's rows,
+    // compute unit u while dequantizing unit u+1, and (inside compute, once the raw stage of unit u+1
+    // is read) start loading unit u+4 into it. Returns false when the range is done.
     auto step = [&](auto kst) __attribute__((always_inline)) -> bool {
         constexpr int K = decltype(kst)::value;
+        constexpr int KR = K % 3, KT = K & 1, KR2 = (K + 1) % 3, KT2 = (K + 1) & 1;
         prefetch_ids();
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * RL));  // own loads of unit u+1 are done
         compiler_fence();
         __builtin_amdgcn_s_barrier();                          // everyone's are; step u-1 is finished
         compiler_fence();
         const uint32_t cur = info[K];
-        const uint32_t nxt = info[(K + 1) & 3];
+        const uint32_t nxt = info[(K + 1) % 6];
         refresh_offsets();
-        issue(std::integral_constant<int, K>{});
         if (__builtin_expect(cc.g == g_begin || cc.k == 0, 0)) begin_segment();
-        compute(std::integral_constant<int, K & 1>{}, cur, std::integral_constant<int, (K + 1) & 3>{},
-                std::integral_constant<int, (K + 1) & 1>{}, nxt);
+        compute(std::integral_constant<int, KT>{}, cur, std::integral_constant<int, KR2>{},
+                std::integral_constant<int, KT2>{}, nxt, std::integral_constant<int, (K + 4) % 6>{});
         if (__builtin_expect(cc.g + 1 == g_end || cc.k + 1 == cc.nu, 0)) end_segment();
         advance(cc, p);
         return cc.g < g_end;
     };
 
-    // Prologue: units 0..3 in flight, unit 0 dequantized. The sparse form first copies the slot
-    // tables of units 0..3 and waits for them.
+    // Prologue: units 0..2 in flight, unit 0 dequantized, then unit 3 in flight in its raw stage. The
+    // sparse form first copies the slot tables of units 0..2 and waits for them.
     if constexpr (SPARSE) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) copy_slot_table();
+        for (int i = 0; i < 3; ++i) copy_slot_table();
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
         lds_barrier();
     }
     prefetch_ids();
-    issue(std::integral_constant<int, 0>{});
+    issue(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     prefetch_ids();
-    issue(std::integral_constant<int, 1>{});
+    issue(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
     prefetch_ids();
-    issue(std::integral_constant<int, 2>{});
-    prefetch_ids();
-    issue(std::integral_constant<int, 3>{});
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * RL));
+    issue(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * RL));
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
@@ -710,12 +742,18 @@ void decode_mla_kernel(MlaDecodeParams p) {
         conv_store(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, info[0], cin, 0,
                    std::integral_constant<int, kLatentIters>{}, true);
     }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));  // own reads of raw stage 0 are done
+    lds_barrier();                                     // everyone's are
+    prefetch_ids();
+    issue(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
 
     while (true) {
         if (!step(std::integral_constant<int, 0>{})) break;
         if (!step(std::integral_constant<int, 1>{})) break;
         if (!step(std::integral_constant<int, 2>{})) break;
         if (!step(std::integral_constant<int, 3>{})) break;
+        if (!step(std::integral_constant<int, 4>{})) break;
+        if (!step(std::integral_constant<int, 5>{})) break;
     }
     // Drain: the loads issued for units past the range still target this work-group's LDS.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));

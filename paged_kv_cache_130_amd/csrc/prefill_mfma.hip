@@ -9,9 +9,14 @@
 // paged_attention), for every row of the chunk.
 //
 // Mapping: the rows of one K/V head are the (position, query head) pairs of the chunk,
-// position-major. A work-group owns 128 of them (4 waves x two 16-row tiles) and walks the paged
-// context in 64-token K/V tiles, which its waves copy from HBM straight into LDS (lds_dma,
-// two stages: the next tile is in flight while one is computed) and then share. Per tile and row
+// position-major. A work-group owns 128 of them and walks their causal range of the paged context
+// in 64-token K/V tiles. Its 8 waves form two groups of 4 (each wave two 16-row tiles of the 128
+// rows): group 0 takes the first half of the range's tiles and group 1 the second half, each
+// copying its tiles from HBM straight into its own LDS stages (lds_dma, two stages per group: the
+// next tile is in flight while one is computed) shared by its 4 waves; at the end group 1 hands its
+// (m, l, O) to group 0 through LDS and group 0 merges them (log-sum-exp) and writes the rows. The
+// causal ranges of a chunk's row blocks grow from one tile to the whole context, so halving the
+// long ones evens out the work-groups of a launch. Per tile and row
 // tile: S^T = K . Q^T on v_mfma_f32_16x16x32 (K from LDS, the rows' queries held in registers as the
 // B columns), causal and context masks, lazily rescaled online softmax, and O += P . V on
 // v_mfma_f32_16x16x32 with the value operand read through ds_read_b64_tr_b16 (the operand orders of
@@ -76,13 +81,15 @@ constexpr int kPT = 64;                    // tokens per K/V tile
 constexpr int kPRow = kD * 2;              // bytes of one K/V head row
 constexpr int kPStage = kPT * kPRow;       // 16 KB
 constexpr int kPRows = 128;                // query rows per work-group
+constexpr int kPWaves = 8;                 // waves per chunk work-group: two groups of 4
 
-// K and V tiles, two stages each, as separate objects (see decode_mla.hip: the compiler then tells
-// the stage being read from the one being filled by the direct-to-LDS copies).
-__shared__ __attribute__((aligned(16))) char s_pk0[kPStage];
-__shared__ __attribute__((aligned(16))) char s_pk1[kPStage];
-__shared__ __attribute__((aligned(16))) char s_pv0[kPStage];
-__shared__ __attribute__((aligned(16))) char s_pv1[kPStage];
+// K and V tiles, two stages each and one copy per wave group ([group][tile] inside each object), as
+// separate objects per stage (see decode_mla.h: the compiler then tells the stage being read from
+// the one being filled by the direct-to-LDS copies).
+__shared__ __attribute__((aligned(16))) char s_pk0[2 * kPStage];
+__shared__ __attribute__((aligned(16))) char s_pk1[2 * kPStage];
+__shared__ __attribute__((aligned(16))) char s_pv0[2 * kPStage];
+__shared__ __attribute__((aligned(16))) char s_pv1[2 * kPStage];
 
 template <int K>
 __device__ __forceinline__ char* pk_stage() {
@@ -103,7 +110,10 @@ __device__ __forceinline__ int pswz(int r) { return (((r >> 2) & 3) << 1) | (r &
 // One work-group's item of the chunk rows (item = (sequence, row block) index * Hkv + K/V head).
 template <bool BF16>
 __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int item) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0..7
+    const int grp = wave >> 2;                                           // tile half of this wave's group
+    const int wv = wave & 3;                                             // wave within the group
+    const int gtid = threadIdx.x & 255;                                  // thread within the group
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4;
     const int c = lane & 15;
@@ -123,12 +133,16 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
     const int wg_r0 = rb * kPRows;
     const int wg_rend = min(R, wg_r0 + kPRows);
     const int wg_amax = n - qlen + (wg_rend - 1) / G;      // causal limit of the work-group's last row
-    const int r0 = wg_r0 + 32 * wave;                      // this wave's rows
+    const int r0 = wg_r0 + 32 * wv;                        // this wave's rows
     const int rend = min(wg_rend, r0 + 32);
     const int a_max = r0 < rend ? n - qlen + (rend - 1) / G : -1;
     const int hq0 = kvh * G;
     const int ntiles = wg_amax >= 0 ? wg_amax / kPT + 1 : 0;
-    const int wave_tiles = a_max >= 0 ? a_max / kPT + 1 : 0;
+    const int wave_tiles = a_max >= 0 ? a_max / kPT + 1 : 0;  // tiles holding this wave's visible tokens
+    // Tile halves: group 0 takes tiles [0, mid), group 1 [mid, ntiles); both run mid steps.
+    const int mid = (ntiles + 1) >> 1;
+    const int jbeg = grp == 0 ? 0 : mid;
+    const int jend = grp == 0 ? mid : ntiles;
 
     // Per row tile: Q of row r0 + 16nt + c as the B operand, and that row's causal limit.
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(p.q);
@@ -165,8 +179,9 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
             trbase[d3] = (g4 + 4 * j) * kPRow + ((2 * (d3 ^ j) + (h ^ (g4 & 1))) << 4) + ((c & 1) << 3);
     }
 
-    // Copies: wave w loads tokens [16w, 16w + 16) of a tile, four rows per load instruction: lane i
-    // fills LDS chunk i % 16 of row 16w + 4r + i / 16 with global chunk (i % 16) ^ pswz(row).
+    // Copies: wave w of a group loads tokens [16w, 16w + 16) of the group's tile, four rows per load
+    // instruction: lane i fills LDS chunk i % 16 of row 16w + 4r + i / 16 with global chunk
+    // (i % 16) ^ pswz(row).
     const int64_t krow = p.k_row_bytes, vrow = p.v_row_bytes;
     const uint32_t nb = (uint32_t)p.num_blocks;
     const int32_t* bt = p.block_tables + (size_t)s * p.bt_stride;
@@ -174,7 +189,7 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
     int dma_row[4], dma_chunk[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        dma_row[r] = 16 * wave + 4 * r + (lane >> 4);
+        dma_row[r] = 16 * wv + 4 * r + (lane >> 4);
         dma_chunk[r] = (lane & 15) ^ pswz(dma_row[r]);
     }
     // Block id of this wave's 16 tokens of tile j, and whether each 16-token group of the tile holds
@@ -187,12 +202,12 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
     auto prefetch = [&](int j) __attribute__((always_inline)) {
         pre_ok = 0;
         pre_phys = -1;
-        if (j < ntiles) {
+        if (j < jend) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int id = group_id(j, g);
                 if ((uint32_t)id < nb) pre_ok |= 1 << g;
-                if (g == wave) pre_phys = id;
+                if (g == wv) pre_phys = id;
             }
         }
     };
@@ -200,9 +215,9 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
     auto issue = [&](auto kst, int j) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
         tile_ok[K] = pre_ok;
-        char* ks_ = pk_stage<K>();
-        char* vs_ = pv_stage<K>();
-        if (pre_ok & (1 << wave)) {
+        char* ks_ = pk_stage<K>() + grp * kPStage;
+        char* vs_ = pv_stage<K>() + grp * kPStage;
+        if (pre_ok & (1 << wv)) {
             const int64_t phys = pre_phys;
             const char* kb = p.k + phys * p.k_block_stride + (int64_t)kvh * kPRow;
             const char* vb = p.v + phys * p.v_block_stride + (int64_t)kvh * kPRow;
@@ -211,8 +226,8 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
                 const int64_t row_in_block = (j * kPT + dma_row[r]) & (bs - 1);
                 const char* ksrc = kb + row_in_block * krow + dma_chunk[r] * 16;
                 const char* vsrc = vb + row_in_block * vrow + dma_chunk[r] * 16;
-                lds_dma<16>(ksrc, lds_addr(ks_) + (16 * wave + 4 * r) * kPRow);
-                lds_dma<16>(vsrc, lds_addr(vs_) + (16 * wave + 4 * r) * kPRow);
+                lds_dma<16>(ksrc, lds_addr(ks_) + (16 * wv + 4 * r) * kPRow);
+                lds_dma<16>(vsrc, lds_addr(vs_) + (16 * wv + 4 * r) * kPRow);
             }
         } else {
             // No context tokens here, or an invalid block id: the scores are masked; the value rows
@@ -237,8 +252,8 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
 
     auto compute = [&](auto kst, int j) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
-        const char* kt = pk_stage<K>();
-        const char* vt = pv_stage<K>();
+        const char* kt = pk_stage<K>() + grp * kPStage;
+        const char* vt = pv_stage<K>() + grp * kPStage;
         const int t0 = j * kPT;
         const int okb = tile_ok[K];
 
@@ -349,62 +364,108 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
         }
     };
 
-    auto step = [&](auto kst, int j) __attribute__((always_inline)) {
+    // Step jrel of both groups: group 0 on tile jrel, group 1 on tile mid + jrel (if still in its
+    // range). Every barrier is reached by all 8 waves.
+    auto step = [&](auto kst, int jrel) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
+        const int j = jbeg + jrel;
+        const bool live = j < jend;
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // this wave's copies of tile j are in
-        lds_barrier();                                      // everyone's are; tile j - 1 is done
-        if (j * kPT + kPT > n) {
-            // The last tile reaches past the context: zero the value rows past it (the copies brought
-            // whatever the block holds there).
-            char* vs_ = pv_stage<K>();
-            for (int x = threadIdx.x; x < kPT * 16; x += 256) {
-                const int row = x >> 4;
-                if (j * kPT + row >= n) *reinterpret_cast<uint4*>(vs_ + row * kPRow + ((x & 15) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+        lds_barrier();                                      // everyone's are; the previous tile is done
+        // A tile reaching past the context: zero its value rows past it (the copies brought whatever
+        // the block holds there). The condition covers both groups' tiles, so the barrier is uniform.
+        const bool z0 = jrel < mid && (jrel + 1) * kPT > n;
+        const bool z1 = mid + jrel < ntiles && (mid + jrel + 1) * kPT > n;
+        if (z0 || z1) {
+            if (live && (j + 1) * kPT > n) {
+                char* vs_ = pv_stage<K>() + grp * kPStage;
+                for (int x = gtid; x < kPT * 16; x += 256) {
+                    const int row = x >> 4;
+                    if (j * kPT + row >= n) *reinterpret_cast<uint4*>(vs_ + row * kPRow + ((x & 15) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+                }
             }
             __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
             lds_barrier();
         }
-        if (j + 1 < ntiles) issue(std::integral_constant<int, K ^ 1>{}, j + 1);
-        if (j < wave_tiles) compute(kst, j);
+        if (j + 1 < jend) issue(std::integral_constant<int, K ^ 1>{}, j + 1);
+        if (live && j < wave_tiles) compute(kst, j);
         // The block ids of tile j + 2, read after the products: scalar loads share their wait counter
         // with LDS reads, so issued before the score phase they would stall its first LDS wait.
         prefetch(j + 2);
     };
 
-    if (ntiles > 0) {
-        prefetch(0);
-        issue(std::integral_constant<int, 0>{}, 0);
-        prefetch(1);
-        for (int j = 0; j < ntiles; j += 2) {
-            step(std::integral_constant<int, 0>{}, j);
-            if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
+    if (mid > 0) {
+        prefetch(jbeg);
+        if (jbeg < jend) issue(std::integral_constant<int, 0>{}, jbeg);
+        prefetch(jbeg + 1);
+        for (int jrel = 0; jrel < mid; jrel += 2) {
+            step(std::integral_constant<int, 0>{}, jrel);
+            if (jrel + 1 < mid) step(std::integral_constant<int, 1>{}, jrel + 1);
         }
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
+    // Row sums over the four lane groups: row 16 nt + c in lane c.
+    float lt[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        lt[nt] = l[nt];
+        lt[nt] += __shfl_xor(lt[nt], 16);
+        lt[nt] += __shfl_xor(lt[nt], 32);
+    }
+    // Group 1 hands (m, l, O) of its rows to group 0 through the K and V stages, which are free once
+    // every wave has passed its last product (the barrier below).
+    lds_barrier();
+    float* xo = reinterpret_cast<float*>(wv < 2 ? s_pk0 : s_pk1) + (wv & 1) * (32 * kD);  // 32 rows x 128
+    float* xm = reinterpret_cast<float*>(s_pv0) + wv * 64;                                  // 32 rows x (m, l)
+    if (grp == 1) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) xo[(16 * nt + 4 * g4 + jj) * kD + 16 * dt + c] = O[nt][dt][jj];
+            if (g4 == 0) {
+                xm[2 * (16 * nt + c)] = m[nt];
+                xm[2 * (16 * nt + c) + 1] = lt[nt];
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    lds_barrier();
+    if (grp == 1) return;
+
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        float lt = l[nt];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        // Weights of the two halves for row 16 nt + c: 2^(m_i - M) with M the larger reference (a
+        // half without visible tokens has m = -inf and weight 0).
+        const float m1 = xm[2 * (16 * nt + c)];
+        const float l1 = xm[2 * (16 * nt + c) + 1];
+        const float M = fmaxf(m[nt], m1);
+        const float w0 = m[nt] == M ? 1.f : fast_exp2(m[nt] - M);
+        const float w1 = m1 == M ? 1.f : fast_exp2(m1 - M);
+        const float Lc = w0 * lt[nt] + w1 * l1;
+        const float inv_c = Lc > 0.f ? 1.f / Lc : 0.f;  // no visible token (inconsistent lengths): output 0
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int r = r0 + 16 * nt + 4 * g4 + jj;
-            const float L = __shfl(lt, 4 * g4 + jj);
+            const float a0 = __shfl(w0 * inv_c, 4 * g4 + jj);
+            const float a1 = __shfl(w1 * inv_c, 4 * g4 + jj);
             if (r >= rend) continue;
             const int pos = r / G;
             const int head = r - pos * G;
-            const float inv = L > 0.f ? 1.f / L : 0.f;  // no visible token (inconsistent lengths): output 0
             uint16_t* o = out + ((size_t)(q0 + pos) * p.num_q_heads + hq0 + head) * kD + c;
+            const float* x1 = xo + (16 * nt + 4 * g4 + jj) * kD + c;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[16 * dt] = (uint16_t)(pack2<BF16>(O[nt][dt][jj] * inv, 0.f) & 0xFFFFu);
+            for (int dt = 0; dt < 8; ++dt)
+                o[16 * dt] = (uint16_t)(pack2<BF16>(fmaf(O[nt][dt][jj], a0, x1[16 * dt] * a1), 0.f) & 0xFFFFu);
         }
     }
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(PrefillParams p) {
     prefill_block<BF16>(p, blockIdx.x);
 }
 
@@ -414,10 +475,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // alternate in dispatch order while both last (even = chunk rows, odd = decode rows); of the orders
 // measured (chunk rows first, alternating singly, alternating in runs of 8), this one gives the
 // shortest call when the chunk rows alone fill every CU, and the same total over both steps of a
-// chunked prompt. Both kinds fit the same budget: two waves per SIMD, and the chunk rows' LDS tiles
-// limit a CU to two work-groups, which is also the decode waves' register-limited occupancy.
+// chunked prompt. Both kinds fit the same budget: 8 waves per work-group, two waves per SIMD; the
+// chunk rows' LDS tiles (128 KB) limit a CU to one work-group, which is also the decode waves'
+// register-limited occupancy.
 template <bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mixed_chunk_kernel(
+__global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void mixed_chunk_kernel(
     PrefillParams pp, DenseDecodeParams dp, int prefill_wgs, int decode_wgs) {
     const int both = min(prefill_wgs, decode_wgs);
     int b = blockIdx.x;
@@ -434,7 +496,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         prefill_block<BF16>(pp, b);
     } else {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        decode_mfma_wave<BF16>(dp, b * 4 + wave);
+        decode_mfma_wave<BF16>(dp, b * kPWaves + wave);
     }
 }
 
@@ -454,23 +516,23 @@ hipError_t launch_prefill_chunk(const PrefillParams& p, hipStream_t stream) {
     const int64_t wgs = prefill_wgs(p);
     if (wgs <= 0) return hipSuccess;
     if (p.is_bf16)
-        hipLaunchKernelGGL((prefill_mfma_kernel<true>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((prefill_mfma_kernel<true>), dim3((unsigned)wgs), dim3(64 * kPWaves), 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_mfma_kernel<false>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((prefill_mfma_kernel<false>), dim3((unsigned)wgs), dim3(64 * kPWaves), 0, stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_mixed_chunk(const PrefillParams& pp, const DenseDecodeParams& dp, hipStream_t stream) {
     const int64_t pw = pp.num_seqs > 0 ? prefill_wgs(pp) : 0;
-    const int64_t dw = ((int64_t)dp.num_kv_heads * dp.num_seqs * dp.max_parts + 3) / 4;
+    const int64_t dw = ((int64_t)dp.num_kv_heads * dp.num_seqs * dp.max_parts + kPWaves - 1) / kPWaves;
     if (pw + dw <= 0) return hipSuccess;
     if (pw + dw > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (pp.is_bf16)
-        hipLaunchKernelGGL((mixed_chunk_kernel<true>), dim3((unsigned)(pw + dw)), dim3(256), 0, stream, pp, dp, (int)pw,
-                           (int)dw);
+        hipLaunchKernelGGL((mixed_chunk_kernel<true>), dim3((unsigned)(pw + dw)), dim3(64 * kPWaves), 0, stream, pp,
+                           dp, (int)pw, (int)dw);
     else
-        hipLaunchKernelGGL((mixed_chunk_kernel<false>), dim3((unsigned)(pw + dw)), dim3(256), 0, stream, pp, dp,
-                           (int)pw, (int)dw);
+        hipLaunchKernelGGL((mixed_chunk_kernel<false>), dim3((unsigned)(pw + dw)), dim3(64 * kPWaves), 0, stream, pp,
+                           dp, (int)pw, (int)dw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || dp.max_parts <= 1) return e;
     return launch_decode_reduce(dp, stream);

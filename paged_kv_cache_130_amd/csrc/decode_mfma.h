@@ -143,11 +143,16 @@ __device__ __forceinline__ void decode_mfma_wave(const DenseDecodeParams& p, int
     const int tb = part * P;
     const int te = min(ctx, tb + P);
 
-    // Q as the B operand of the score MFMA: lane (g4, c) holds head c, dims 32*ks + 8*g4 .. +7.
+    // Q as the B operand of the score MFMA: lane (g4, c) holds head c, dims 32*ks + 8*g4 .. +7 for
+    // 16-bit rows. For FP8 rows the k order is permuted so that a lane's K operands of k-steps 2h and
+    // 2h+1 are 16 consecutive codes (one 16-byte load): dims 64*(ks/2) + 16*g4 + 8*(ks%2) .. +7. The
+    // order of k inside a product is free as long as both operands follow it.
     uint4 qb[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        qb[ks] = c < G ? *reinterpret_cast<const uint4*>(qrow + c * kD + 32 * ks + 8 * g4) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) {
+        const int d0 = FP8 ? 64 * (ks >> 1) + 16 * g4 + 8 * (ks & 1) : 32 * ks + 8 * g4;
+        qb[ks] = c < G ? *reinterpret_cast<const uint4*>(qrow + c * kD + d0) : make_uint4(0, 0, 0, 0);
+    }
 
     const int tpb_log2 = p.tiles_per_block_log2;
     const int tpb_mask = (1 << tpb_log2) - 1;
@@ -157,8 +162,9 @@ __device__ __forceinline__ void decode_mfma_wave(const DenseDecodeParams& p, int
     const int tbl = lane < nblk ? bt[lb0 + lane] : 0;
 
     const int64_t krow = p.k_row_bytes, vrow = p.v_row_bytes;
-    // K: token sigma(c), dims 8*g4 (+32 per k-step); V: token g4 (+4 per load), dims 8*c.
-    const uint32_t klane = (uint32_t)(kvh * (kD * kEsz) + 8 * kEsz * g4) + (uint32_t)sigma(c) * (uint32_t)krow;
+    // K: token sigma(c), dims 8*g4 (+32 per k-step), or for FP8 dims 16*g4 (+64 per 16-byte load);
+    // V: token g4 (+4 per load), dims 8*c.
+    const uint32_t klane = (uint32_t)(kvh * (kD * kEsz) + (FP8 ? 16 : 8 * kEsz) * g4) + (uint32_t)sigma(c) * (uint32_t)krow;
     const uint32_t vlane = (uint32_t)(kvh * (kD * kEsz) + 8 * kEsz * c) + (uint32_t)g4 * (uint32_t)vrow;
     const uint32_t nb = (uint32_t)p.num_blocks;
     const int ntiles = (te - tb + 15) >> 4;
@@ -181,7 +187,11 @@ __device__ __forceinline__ void decode_mfma_wave(const DenseDecodeParams& p, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if constexpr (FP8) {
-                kk[i] = *reinterpret_cast<const uint2*>(kt + i * kstep + ko);
+                if ((i & 1) == 0) {  // k-steps i and i + 1: one 16-byte load
+                    const uint4 w = *reinterpret_cast<const uint4*>(kt + (real ? 64 * (i >> 1) : 0) + ko);
+                    kk[i] = make_uint2(w.x, w.y);
+                    kk[i + 1] = make_uint2(w.z, w.w);
+                }
                 vv[i] = load_nt8(vt + i * vstep + vo);
             } else {
                 kk[i] = *reinterpret_cast<const uint4*>(kt + i * kstep + ko);

@@ -136,6 +136,7 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
     const int r0 = wg_r0 + 32 * wv;                        // this wave's rows
     const int rend = min(wg_rend, r0 + 32);
     const int a_max = r0 < rend ? n - qlen + (rend - 1) / G : -1;
+    const int amin = n - qlen + r0 / G;                    // causal limit of this wave's first row
     const int hq0 = kvh * G;
     const int ntiles = wg_amax >= 0 ? wg_amax / kPT + 1 : 0;
     const int wave_tiles = a_max >= 0 ? a_max / kPT + 1 : 0;  // tiles holding this wave's visible tokens
@@ -278,25 +279,38 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) S[sub][nt] = mfma_k32<BF16>(abuf[sub][ks], qb[nt][ks], S[sub][nt]);
 
-        // Register jj of sub-tile sub holds token t0 + 16 sub + g4 + 4 jj of row c.
+        // Register jj of sub-tile sub holds token t0 + 16 sub + g4 + 4 jj of row c. A tile inside
+        // every row's causal range with all four 16-token groups in valid blocks needs no masks (the
+        // wave's first row has the shortest range).
+        const bool full = okb == 15 && t0 + kPT - 1 <= amin;
         uint4 Ahi[2][2], Alo[2][2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             bool ok[4][4];
             float mx = kNegInf;
+            if (full) {
 #pragma unroll
-            for (int sub = 0; sub < 4; ++sub)
+                for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int t = t0 + 16 * sub + g4 + 4 * jj;
-                    ok[sub][jj] = ((okb >> sub) & 1) && t <= alim[nt];
-                    mx = ok[sub][jj] ? fmaxf(mx, S[sub][nt][jj]) : mx;
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float tmax = mx * sl2;
-            const bool need = tmax > m[nt] + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                    for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, S[sub][nt][jj]);
+            } else {
+#pragma unroll
+                for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int t = t0 + 16 * sub + g4 + 4 * jj;
+                        ok[sub][jj] = ((okb >> sub) & 1) && t <= alim[nt];
+                        mx = ok[sub][jj] ? fmaxf(mx, S[sub][nt][jj]) : mx;
+                    }
+            }
+            // The reference m is the same in the four lane groups of a row, so a row must move it
+            // exactly when one of its lane groups' maxima exceeds it by the slack: the row maxima
+            // (two cross-lane steps) are formed only then.
+            if (__builtin_amdgcn_ballot_w64(mx * sl2 > m[nt] + kRescaleSlack) != 0) {
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float tmax = mx * sl2;
+                const bool need = tmax > m[nt] + kRescaleSlack;
                 const float mnew = need ? tmax : m[nt];
                 const float alpha = need ? fast_exp2(m[nt] - mnew) : 1.f;
                 l[nt] *= alpha;
@@ -312,7 +326,7 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const float ex = fast_exp2(fmaf(S[sub][nt][jj], sl2, -m[nt]));
-                    pr[sub][jj] = ok[sub][jj] ? ex : 0.f;
+                    pr[sub][jj] = full || ok[sub][jj] ? ex : 0.f;
                     l[nt] += pr[sub][jj];
                 }
 #pragma unroll
@@ -469,29 +483,20 @@ __global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2,
     prefill_block<BF16>(p, blockIdx.x);
 }
 
-// A mixed call in one launch: some work-groups take the chunk rows, the others the decode rows on the
-// grouped-query decode waves. The chunk rows are bound by the matrix cores and the decode rows by
-// HBM, so running them side by side hides part of the shorter behind the longer. The two kinds
-// alternate in dispatch order while both last (even = chunk rows, odd = decode rows); of the orders
-// measured (chunk rows first, alternating singly, alternating in runs of 8), this one gives the
-// shortest call when the chunk rows alone fill every CU, and the same total over both steps of a
-// chunked prompt. Both kinds fit the same budget: 8 waves per work-group, two waves per SIMD; the
-// chunk rows' LDS tiles (128 KB) limit a CU to one work-group, which is also the decode waves'
-// register-limited occupancy.
+// A mixed call in one launch: the first work-groups take the decode rows on the grouped-query decode
+// waves, the rest the chunk rows. Both kinds fit the same budget: 8 waves per work-group, two waves
+// per SIMD; the chunk rows' LDS tiles (128 KB) limit a CU to one work-group, which is also the
+// decode waves' register-limited occupancy, so the decode rows stream from HBM as they would alone
+// and the chunk rows take over each CU as its decode work-groups retire. Of the orders measured
+// (decode rows first, chunk rows first, alternating singly or in runs of 8) this one gives the
+// shortest call: interleaving the two kinds leaves half the CUs streaming decode rows, and the
+// register-limited decode waves of one CU cannot keep enough loads in flight to make up for it.
 template <bool BF16>
 __global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void mixed_chunk_kernel(
-    PrefillParams pp, DenseDecodeParams dp, int prefill_wgs, int decode_wgs) {
-    const int both = min(prefill_wgs, decode_wgs);
+    PrefillParams pp, DenseDecodeParams dp, int decode_wgs) {
     int b = blockIdx.x;
-    bool chunk;
-    if (b < 2 * both) {
-        chunk = (b & 1) == 0;
-        b >>= 1;
-    } else {
-        b -= 2 * both;
-        chunk = b < prefill_wgs - both;
-        b = both + (chunk ? b : b - (prefill_wgs - both));
-    }
+    const bool chunk = b >= decode_wgs;
+    if (chunk) b -= decode_wgs;
     if (chunk) {
         prefill_block<BF16>(pp, b);
     } else {
@@ -529,10 +534,10 @@ hipError_t launch_mixed_chunk(const PrefillParams& pp, const DenseDecodeParams& 
     if (pw + dw > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (pp.is_bf16)
         hipLaunchKernelGGL((mixed_chunk_kernel<true>), dim3((unsigned)(pw + dw)), dim3(64 * kPWaves), 0, stream, pp,
-                           dp, (int)pw, (int)dw);
+                           dp, (int)dw);
     else
         hipLaunchKernelGGL((mixed_chunk_kernel<false>), dim3((unsigned)(pw + dw)), dim3(64 * kPWaves), 0, stream, pp,
-                           dp, (int)pw, (int)dw);
+                           dp, (int)dw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || dp.max_parts <= 1) return e;
     return launch_decode_reduce(dp, stream);

@@ -12,11 +12,13 @@
 // position-major. A work-group owns 128 of them and walks their causal range of the paged context
 // in 64-token K/V tiles. Its 8 waves form two groups of 4 (each wave two 16-row tiles of the 128
 // rows): group 0 takes the first half of the range's tiles and group 1 the second half, each
-// copying its tiles from HBM straight into its own LDS stages (lds_dma, two stages per group: the
-// next tile is in flight while one is computed) shared by its 4 waves; at the end group 1 hands its
-// (m, l, O) to group 0 through LDS and group 0 merges them (log-sum-exp) and writes the rows. The
-// causal ranges of a chunk's row blocks grow from one tile to the whole context, so halving the
-// long ones evens out the work-groups of a launch. Per tile and row
+// copying its tiles from HBM straight into its own LDS stages (lds_dma; the next tile is in flight
+// while one is computed) shared by its 4 waves; at the end group 1 hands its (m, l, O) to group 0
+// through LDS and group 0 merges them (log-sum-exp) and writes the rows. The causal ranges of a
+// chunk's row blocks grow from one tile to the whole context, so halving the long ones evens out the
+// work-groups of a launch. The two waves that share a SIMD belong to different groups, and group 1
+// runs its value products one step behind its scores, so that one wave's softmax (VALU) meets the
+// other's products (matrix core) rather than its own softmax. Per tile and row
 // tile: S^T = K . Q^T on v_mfma_f32_16x16x32 (K from LDS, the rows' queries held in registers as the
 // B columns), causal and context masks, lazily rescaled online softmax, and O += P . V on
 // v_mfma_f32_16x16x32 with the value operand read through ds_read_b64_tr_b16 (the operand orders of
@@ -83,23 +85,27 @@ constexpr int kPStage = kPT * kPRow;       // 16 KB
 constexpr int kPRows = 128;                // query rows per work-group
 constexpr int kPWaves = 8;                 // waves per chunk work-group: two groups of 4
 
-// K and V tiles, two stages each and one copy per wave group ([group][tile] inside each object), as
-// separate objects per stage (see decode_mla.h: the compiler then tells the stage being read from
-// the one being filled by the direct-to-LDS copies).
+// K and V tiles: two K stages per wave group ([group][tile] inside each object, as separate objects
+// per stage, see decode_mla.h), two V stages for group 0 and three for group 1 (s_pv0 and s_pv1
+// hold [group][tile], s_pv2 group 1's third stage): group 1 multiplies a tile's values one step
+// after its scores.
 __shared__ __attribute__((aligned(16))) char s_pk0[2 * kPStage];
 __shared__ __attribute__((aligned(16))) char s_pk1[2 * kPStage];
 __shared__ __attribute__((aligned(16))) char s_pv0[2 * kPStage];
 __shared__ __attribute__((aligned(16))) char s_pv1[2 * kPStage];
+__shared__ __attribute__((aligned(16))) char s_pv2[kPStage];
 
 template <int K>
 __device__ __forceinline__ char* pk_stage() {
     if constexpr (K == 0) return s_pk0;
     else return s_pk1;
 }
-template <int K>
-__device__ __forceinline__ char* pv_stage() {
-    if constexpr (K == 0) return s_pv0;
-    else return s_pv1;
+// V stage of the group's tile jrel (its jrel-th step): group 0 alternates two stages, group 1 cycles
+// through three.
+__device__ __forceinline__ char* pv_stage(int grp, int jrel) {
+    if (grp == 0) return (jrel & 1) ? s_pv1 : s_pv0;
+    const int r = jrel % 3;
+    return r == 0 ? s_pv0 + kPStage : r == 1 ? s_pv1 + kPStage : s_pv2;
 }
 
 // Swizzle of the 16-byte chunks of tile row r (256-byte rows, a multiple of the 128-byte bank cycle):
@@ -199,27 +205,25 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
         const int t = j * kPT + 16 * g;
         return t < n ? load_scalar(bt + (t >> bs_log2)) : -1;
     };
-    int pre_ok = 0, pre_phys = -1;  // the next tile to copy: validity bits, this wave's block
+    // Block ids of the next tile to copy, one per 16-token group (-1: past the context). They are
+    // only loaded here; the checks that use them wait for the loads in the next step, after its
+    // barrier, so the scalar loads' latency is hidden behind the barrier.
+    int pre_id[4] = {-1, -1, -1, -1};
     auto prefetch = [&](int j) __attribute__((always_inline)) {
-        pre_ok = 0;
-        pre_phys = -1;
-        if (j < jend) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int id = group_id(j, g);
-                if ((uint32_t)id < nb) pre_ok |= 1 << g;
-                if (g == wv) pre_phys = id;
-            }
-        }
+        for (int g = 0; g < 4; ++g) pre_id[g] = j < jend ? group_id(j, g) : -1;
     };
     int tile_ok[2] = {0, 0};
     auto issue = [&](auto kst, int j) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
+        int pre_ok = 0;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) pre_ok |= ((uint32_t)pre_id[g] < nb ? 1 : 0) << g;
         tile_ok[K] = pre_ok;
         char* ks_ = pk_stage<K>() + grp * kPStage;
-        char* vs_ = pv_stage<K>() + grp * kPStage;
+        char* vs_ = pv_stage(grp, j - jbeg);
         if (pre_ok & (1 << wv)) {
-            const int64_t phys = pre_phys;
+            const int64_t phys = pre_id[wv];
             const char* kb = p.k + phys * p.k_block_stride + (int64_t)kvh * kPRow;
             const char* vb = p.v + phys * p.v_block_stride + (int64_t)kvh * kPRow;
 #pragma unroll
@@ -251,39 +255,42 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
     }
     const float sl2 = p.scale_log2;
 
-    auto compute = [&](auto kst, int j) __attribute__((always_inline)) {
+    // Probabilities of the last scored tile as the A operand of its value product (hi and lo parts).
+    uint4 Ahi[2][2], Alo[2][2];
+    auto scores = [&](auto kst, int j) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
         const char* kt = pk_stage<K>() + grp * kPStage;
-        const char* vt = pv_stage<K>() + grp * kPStage;
         const int t0 = j * kPT;
         const int okb = tile_ok[K];
 
-        // Scores for the four 16-token sub-tiles: all 16 K operands are loaded first, then the products
-        // run k-step by k-step over the eight (sub-tile, row tile) accumulators, so consecutive products
-        // are independent.
+        // Scores for the four 16-token sub-tiles, k-step by k-step over the eight (sub-tile, row tile)
+        // accumulators (consecutive products independent); the K operands of the next k-step are
+        // read while the current one's products run.
         f32x4_t S[4][2];
-        uint4 abuf[4][4];
+        uint4 abuf[2][4];
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                abuf[sub][ks] = *reinterpret_cast<const uint4*>(kt + sub * 16 * kPRow + a_off[ks]);
+        for (int sub = 0; sub < 4; ++sub) abuf[0][sub] = *reinterpret_cast<const uint4*>(kt + sub * 16 * kPRow + a_off[0]);
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) S[sub][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) {
+#pragma unroll
+                for (int sub = 0; sub < 4; ++sub)
+                    abuf[(ks + 1) & 1][sub] = *reinterpret_cast<const uint4*>(kt + sub * 16 * kPRow + a_off[ks + 1]);
+            }
 #pragma unroll
             for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) S[sub][nt] = mfma_k32<BF16>(abuf[sub][ks], qb[nt][ks], S[sub][nt]);
+                for (int nt = 0; nt < 2; ++nt) S[sub][nt] = mfma_k32<BF16>(abuf[ks & 1][sub], qb[nt][ks], S[sub][nt]);
+        }
 
         // Register jj of sub-tile sub holds token t0 + 16 sub + g4 + 4 jj of row c. A tile inside
         // every row's causal range with all four 16-token groups in valid blocks needs no masks (the
         // wave's first row has the shortest range).
         const bool full = okb == 15 && t0 + kPT - 1 <= amin;
-        uint4 Ahi[2][2], Alo[2][2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             bool ok[4][4];
@@ -340,7 +347,10 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
                 Alo[nt][h] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
             }
         }
+    };
 
+    // O += P . V for the tile whose values are at vt, with P in Ahi / Alo.
+    auto pv = [&](const char* vt) __attribute__((always_inline)) {
         // PV over the two 32-token halves h: B operand of dims [16dt, 16dt + 16) is two transposed
         // reads (sub-tiles 2h and 2h + 1).
         auto load_b = [&](int h, int dt) __attribute__((always_inline)) {
@@ -379,36 +389,56 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
     };
 
     // Step jrel of both groups: group 0 on tile jrel, group 1 on tile mid + jrel (if still in its
-    // range). Every barrier is reached by all 8 waves.
-    auto step = [&](auto kst, int jrel) __attribute__((always_inline)) {
-        constexpr int K = decltype(kst)::value;
-        const int j = jbeg + jrel;
-        const bool live = j < jend;
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // this wave's copies of tile j are in
-        lds_barrier();                                      // everyone's are; the previous tile is done
-        // A tile reaching past the context: zero its value rows past it (the copies brought whatever
-        // the block holds there). The condition covers both groups' tiles, so the barrier is uniform.
-        const bool z0 = jrel < mid && (jrel + 1) * kPT > n;
-        const bool z1 = mid + jrel < ntiles && (mid + jrel + 1) * kPT > n;
-        if (z0 || z1) {
-            if (live && (j + 1) * kPT > n) {
-                char* vs_ = pv_stage<K>() + grp * kPStage;
-                for (int x = gtid; x < kPT * 16; x += 256) {
-                    const int row = x >> 4;
-                    if (j * kPT + row >= n) *reinterpret_cast<uint4*>(vs_ + row * kPRow + ((x & 15) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+    // range). Every barrier is reached by all 8 waves. Group 0 scores a tile and multiplies its values
+    // in the same step; group 1 first multiplies the values of the tile it scored in the previous
+    // step, then scores the current one. So the two waves of a SIMD (one per group) are in opposite
+    // phases: while one runs its softmax on the VALU, the other's products keep the matrix core busy.
+    // The loop of one group (G1: group 1), each group with its own copy of the code, so that the
+    // probabilities group 1 carries from one step to the next never meet group 0's register peak.
+    auto run = [&](auto g1) __attribute__((always_inline)) {
+        constexpr bool G1 = decltype(g1)::value;
+        bool have_prev = false;  // group 1: a scored tile still to be multiplied by its values
+        const char* v_prev = s_pv2;
+        auto step = [&](auto kst, int jrel) __attribute__((always_inline)) {
+            constexpr int K = decltype(kst)::value;
+            const int j = jbeg + jrel;
+            const bool live = j < jend;
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // this wave's copies of tile j are in
+            lds_barrier();                                      // everyone's are; the previous tile is done
+            // A tile reaching past the context: zero its value rows past it (the copies brought
+            // whatever the block holds there). The condition covers both groups' tiles, so the
+            // barrier is uniform.
+            const bool z0 = jrel < mid && (jrel + 1) * kPT > n;
+            const bool z1 = mid + jrel < ntiles && (mid + jrel + 1) * kPT > n;
+            if (z0 || z1) {
+                if (live && (j + 1) * kPT > n) {
+                    char* vs_ = pv_stage(grp, jrel);
+                    for (int x = gtid; x < kPT * 16; x += 256) {
+                        const int row = x >> 4;
+                        if (j * kPT + row >= n) *reinterpret_cast<uint4*>(vs_ + row * kPRow + ((x & 15) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+                    }
                 }
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+                lds_barrier();
             }
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-            lds_barrier();
-        }
-        if (j + 1 < jend) issue(std::integral_constant<int, K ^ 1>{}, j + 1);
-        if (live && j < wave_tiles) compute(kst, j);
-        // The block ids of tile j + 2, read after the products: scalar loads share their wait counter
-        // with LDS reads, so issued before the score phase they would stall its first LDS wait.
-        prefetch(j + 2);
-    };
-
-    if (mid > 0) {
+            if (j + 1 < jend) issue(std::integral_constant<int, K ^ 1>{}, j + 1);
+            const bool runs = live && j < wave_tiles;
+            if constexpr (!G1) {
+                if (runs) {
+                    scores(kst, j);
+                    pv(pv_stage(0, jrel));
+                }
+            } else {
+                if (have_prev) pv(v_prev);
+                have_prev = runs;
+                v_prev = pv_stage(1, jrel);
+                if (runs) scores(kst, j);
+            }
+            // The block ids of tile j + 2, read after the products: scalar loads share their wait
+            // counter with LDS reads, so issued before the score phase they would stall its first
+            // LDS wait.
+            prefetch(j + 2);
+        };
         prefetch(jbeg);
         if (jbeg < jend) issue(std::integral_constant<int, 0>{}, jbeg);
         prefetch(jbeg + 1);
@@ -416,6 +446,13 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
             step(std::integral_constant<int, 0>{}, jrel);
             if (jrel + 1 < mid) step(std::integral_constant<int, 1>{}, jrel + 1);
         }
+        if constexpr (G1) {
+            if (have_prev) pv(v_prev);  // the last tile's values
+        }
+    };
+    if (mid > 0) {
+        if (grp == 0) run(std::false_type{});
+        else run(std::true_type{});
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 

@@ -220,13 +220,18 @@ __device__ __forceinline__ void decode_mfma_wave(const DenseDecodeParams& p, int
         }
     };
 
-    Raw k0[4], v0[4], k1[4], v1[4];
-    load(k0, v0, 0);
-    for (int j = 0; j < ntiles; j += 2) {
-        load(k1, v1, j + 1);
-        step(k0, v0, j);
-        load(k0, v0, j + 2);
-        if (j + 1 < ntiles) step(k1, v1, j + 1);
+    // A ring of kDepth tiles: the loads of the next kDepth - 1 tiles are in flight while one is
+    // computed. FP8 tiles are half the bytes, so they keep twice as many in flight.
+    constexpr int kDepth = FP8 ? 4 : 2;
+    Raw kb[kDepth][4], vb[kDepth][4];
+#pragma unroll
+    for (int i = 0; i < kDepth - 1; ++i) load(kb[i], vb[i], i);
+    for (int j = 0; j < ntiles; j += kDepth) {
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+            load(kb[(u + kDepth - 1) % kDepth], vb[(u + kDepth - 1) % kDepth], j + u + kDepth - 1);
+            if (u == 0 || j + u < ntiles) step(kb[u], vb[u], j + u);
+        }
     }
 
     // l summed over the four lane groups gives each head's total; O rows are heads 4*g4 + j.

@@ -6,7 +6,7 @@
 namespace pa {
 
 template <bool BF16, bool FP8>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DenseDecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FP8 ? 3 : 1))) void decode_mfma_kernel(DenseDecodeParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     decode_mfma_wave<BF16, FP8>(p, blockIdx.x * 4 + wave);
 }

@@ -437,6 +437,12 @@ def run_mla(calls, warmup, flush):
     pop = dist(time_calls(torch, lambda: pa.pa_reshape_and_cache(
         case.mla_rows[1], pop_slots, img, mla_v, 1, bs, case.num_blocks, v=case.idx_rows[1], v_cache=img,
         v_view=idx_v), 10, flush))
+    # Reference for the write rates: torch's device copy of the same bytes (the populate reads and
+    # writes ntok x 788 bytes), timed the same way.
+    ref_src = torch.empty(ntok * (656 + 132), dtype=torch.uint8, device="cuda").fill_(7)
+    ref_dst = torch.empty_like(ref_src)
+    ref = dist(time_calls(torch, lambda: ref_dst.copy_(ref_src), 10, flush))
+    del ref_src, ref_dst
     # Quantize-on-write of the same populate: bf16 latent / RoPE / indexer key in, both views written.
     g = torch.Generator(device="cuda")
     g.manual_seed(1305)
@@ -483,6 +489,8 @@ def run_mla(calls, warmup, flush):
         "populate_write_ms_per_layer": pop["median"],
         "populate_write_gbs": ntok * 2 * (656 + 132) / (pop["median"] / 1e3) / 1e9,
         "populate_write_hbm_frac": ntok * 2 * (656 + 132) / (pop["median"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "device_copy_same_bytes_ms": ref["median"],
+        "device_copy_same_bytes_hbm_frac": ntok * 2 * (656 + 132) / (ref["median"] / 1e3) / 1e9 / HBM_PEAK_GBS,
         "quantize_write_ms_per_layer": quant["median"],
         "quantize_write_gbs": quant_bytes / (quant["median"] / 1e3) / 1e9,
         "quantize_write_hbm_frac": quant_bytes / (quant["median"] / 1e3) / 1e9 / HBM_PEAK_GBS,
@@ -710,8 +718,8 @@ def main():
         m = run_mla(MIN_CALLS, 3, flush)
         extra["dsa_mla"] = {k: m[k] for k in ("workload", "sum_context_tokens", "populate_write_ms_per_layer",
                                               "populate_write_gbs", "populate_write_hbm_frac",
-                                              "quantize_write_ms_per_layer", "quantize_write_gbs",
-                                              "quantize_write_hbm_frac", "mla_decode_call_ms",
+                                              "device_copy_same_bytes_hbm_frac", "quantize_write_ms_per_layer",
+                                              "quantize_write_gbs", "quantize_write_hbm_frac", "mla_decode_call_ms",
                                               "mla_decode_call_ms_mean", "mla_decode_call_ms_p10_p90",
                                               "mla_decode_call_ms_warm", "mla_hbm_gbs", "mla_hbm_frac",
                                               "mla_counter_gbs")}

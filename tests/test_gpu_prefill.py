@@ -97,3 +97,44 @@ def test_full_size_long_mixed_sampled(step):
         ref = A.chunk_prefill(sub_q, "bf16", k_img, ov, v_img, ov, 0, tbl[None, :], [n], [0, ql], 16, 8, 128,
                               case.scale, select_rows=set(rows))
         assert_close(got[qsl[s] + np.array(rows)], ref[rows], DENSE_ATOL, DENSE_RTOL, f"seq {s} rows {rows}")
+
+
+# dtype, Hq, Hkv, bs, seq_lens, query_lens: block sizes 128 and 256 (several 64-token tiles per block),
+# row counts that leave a partial last row block, odd tile counts (the second wave group one tile
+# short), ranges of one to three tiles (the second group idle or on a one-token tile), a whole prompt
+# from position 0, and one query head per K/V head (the decode rows then run on the VALU kernel).
+CHUNK_SHAPES = [
+    ("bf16", 8, 2, 128, [1500, 900], [300, 2]),
+    ("f16", 16, 1, 256, [1000, 3], [130, 3]),
+    ("bf16", 12, 4, 16, [1345, 64], [1345, 64]),
+    ("bf16", 4, 4, 32, [700, 65, 9], [70, 2, 1]),
+    ("bf16", 32, 8, 16, [64, 65, 129, 1], [64, 2, 65, 1]),
+]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,bs,seq_lens,query_lens", CHUNK_SHAPES)
+def test_chunk_shapes(dtype, Hq, Hkv, bs, seq_lens, query_lens):
+    need = sum(P.blocks_needed(n, bs) for n in seq_lens)
+    case = workloads.make_chunk_case(seed=2100 + Hq + bs + len(seq_lens), seq_lens=seq_lens, query_lens=query_lens,
+                                     num_blocks=need + 3, num_q_heads=Hq, num_kv_heads=Hkv, dtype=dtype,
+                                     block_size=bs)
+    kh, vh = case.k_pool.clone(), case.v_pool.clone()
+    poison_tails(kh, case.block_tables, case.seq_lens, bs, dtype)
+    poison_tails(vh, case.block_tables, case.seq_lens, bs, dtype)
+    out = run_prefill(case, dev(kh), dev(vh))
+    got = out_to_f64(out, dtype)
+    assert np.isfinite(got).all()
+    ov = oracle_view(case)
+    ref = A.chunk_prefill(bits_np(case.q), dtype, image_of(kh), ov, image_of(vh), ov, 0, case.block_tables,
+                          case.seq_lens, case.query_start_loc, bs, Hkv, 128, case.scale)
+    assert_close(got, ref, DENSE_ATOL, DENSE_RTOL, f"chunk {dtype} {Hq}/{Hkv} bs {bs}")
+
+
+def test_chunk_is_deterministic():
+    """Two calls give the same bits (the wave groups' merge and the delayed value products included)."""
+    case = workloads.make_chunk_case(seed=2200, seq_lens=[900, 300], query_lens=[450, 1], num_blocks=80,
+                                     num_q_heads=16, num_kv_heads=4, dtype="bf16")
+    kd, vd = dev(case.k_pool), dev(case.v_pool)
+    a = run_prefill(case, kd, vd)
+    b = run_prefill(case, kd, vd)
+    assert torch.equal(a, b)

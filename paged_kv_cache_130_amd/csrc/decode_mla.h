@@ -40,8 +40,9 @@
 //    output registers are the PV A operand's token order (sigma of mfma_common.h, two 16-token tiles
 //    per k=32 step); the V operand comes from ds_read_b64_tr_b16, which transposes 4 x 4 blocks of
 //    16-bit values across the lanes of a 16-lane group.
-//  * Per unit: the opening barrier and the exchange barrier; the widening of unit u+1 is
-//    interleaved with the PV products of unit u, and operands are loaded four products ahead. The
+//  * Per unit: the opening barrier and the exchange barrier; the widening of unit u+1 and (dense
+//    form) all but the first of unit u+4's copy instructions are interleaved with the PV products
+//    of unit u, and operands are loaded four products ahead. The
 //    softmax is online (lazy reference, as in the dense decode) and a segment that is not a whole
 //    sequence writes an fp32 partial merged by mla_merge_kernel (log-sum-exp).
 
@@ -286,10 +287,10 @@ void decode_mla_kernel(MlaDecodeParams p) {
 #pragma unroll
     for (int r = 0; r < R; ++r) dma_kk[r] = (r * NW + wave) * 64 + lane;
 
-    // Block ids of unit cl (pre_pb: rows 16..31 when block_size is 16). A step reads them before its
-    // opening wait, which also waits for them, so that their latency is hidden by that wait and no
-    // scalar load is outstanding during the products: scalar loads return out of order, so while
-    // one is pending every wait for LDS data would have to wait for all of it.
+    // Block ids of unit cl (pre_pb: rows 16..31 when block_size is 16). They are read at the end of
+    // a step and waited for by the next step's opening wait, so that no scalar load is outstanding
+    // during the products: scalar loads return out of order, so while one is pending every wait for
+    // LDS data would have to wait for all of it.
     int pre_pa = 0, pre_pb = 0;
     auto prefetch_ids = [&]() __attribute__((always_inline)) {
         if (!SPARSE && cl.g < g_end) {
@@ -312,36 +313,58 @@ void decode_mla_kernel(MlaDecodeParams p) {
         advance(cs, p);
     };
 
-    auto issue_sparse = [&](auto kst, auto kinf) __attribute__((always_inline)) {
+    // The unit whose rows are being copied: its raw stage and where its rows come from (dense: the
+    // block bases and last chunks of rows 0..15 and 16..31; sparse: its slot table and valid rows).
+    // Inside a step of the dense form only the first copy instruction goes out with the unit's issue;
+    // the other R - 1 are spread over the value products, so that the work-group's copies do not all
+    // queue at the address units at once (3% of the call). The sparse form issues them together: its
+    // copies read their slots from LDS, which inside the value products would wait for the prefetched
+    // value operands.
+    uint32_t pend_stage = 0;
+    const char* pend_a = dummy;
+    const char* pend_b = dummy;
+    int pend_lim_a = 0, pend_lim_b = 0;
+    const int32_t* pend_tab = s_slot[0];
+    int pend_v = 0;
+    auto copy_rows = [&](int r) __attribute__((always_inline)) {
+        const int win = r * NW + wave;
+        const int kk = dma_kk[r];
+        const char* src;
+        if constexpr (SPARSE) {
+            const int row = kk / 41;  // >= 32 past the unit's last chunk
+            const int32_t sl = pend_tab[row & 31];
+            const bool ok = row < pend_v && (uint32_t)sl < (uint32_t)p.num_slots;
+            src = ok ? p.kv + (int64_t)(sl >> p.block_size_log2) * p.block_stride +
+                           (int64_t)(sl & (p.block_size - 1)) * kRow + (kk - row * 41) * 16
+                     : dummy;
+        } else {
+            const bool hi = p.block_size < kUnit && kk >= 16 * 41;
+            src = (hi ? pend_b : pend_a) + (int64_t)min(kk, hi ? pend_lim_b : pend_lim_a) * 16;
+        }
+        lds_dma<16>(src, win < kWindows ? pend_stage + win * 1024 : lds_addr(s_junk));
+    };
+
+    auto issue_sparse = [&](auto kst, auto kinf, auto all) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
         constexpr int KI = decltype(kinf)::value;
         const int v = cl.g < g_end ? min(kUnit, cl.ctx - cl.k * kUnit) : 0;
         const int32_t* tab = s_slot[cl.g & 7];
-        const uint32_t nslots = (uint32_t)p.num_slots;
         const int32_t mine = tab[lane & 31];
-        info[KI] = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && lane < v && (uint32_t)mine < nslots);
-        char* stage = raw_stage<K>();
+        info[KI] = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && lane < v && (uint32_t)mine < (uint32_t)p.num_slots);
+        pend_stage = lds_addr(raw_stage<K>());
+        pend_tab = tab;
+        pend_v = v;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int win = r * NW + wave;
-            const int kk = dma_kk[r];
-            const int row = kk / 41;  // >= 32 past the unit's last chunk
-            const int32_t sl = tab[row & 31];
-            const bool ok = row < v && (uint32_t)sl < nslots;
-            const char* src = ok ? p.kv + (int64_t)(sl >> p.block_size_log2) * p.block_stride +
-                                       (int64_t)(sl & (p.block_size - 1)) * kRow + (kk - row * 41) * 16
-                                 : dummy;
-            lds_dma<16>(src, win < kWindows ? lds_addr(stage) + win * 1024 : lds_addr(s_junk));
-        }
+        for (int r = 0; r < (decltype(all)::value ? R : 1); ++r) copy_rows(r);
         copy_slot_table();
         advance(cl, p);
     };
 
-    auto issue = [&](auto kst, auto kinf) __attribute__((always_inline)) {
+    auto issue = [&](auto kst, auto kinf, auto all) __attribute__((always_inline)) {
         constexpr int K = decltype(kst)::value;
         constexpr int KI = decltype(kinf)::value;
         if constexpr (SPARSE) {
-            issue_sparse(kst, kinf);
+            issue_sparse(kst, kinf, all);
             return;
         }
         const bool live = cl.g < g_end;
@@ -377,16 +400,13 @@ void decode_mla_kernel(MlaDecodeParams p) {
             }
         }
         info[KI] = (v >= 32 ? 0xFFFFFFFFu : (1u << v) - 1u) & ((ok_a ? 0xFFFFu : 0u) | (ok_b ? 0xFFFF0000u : 0u));
-        char* stage = raw_stage<K>();
-        const bool split = p.block_size < kUnit;
+        pend_stage = lds_addr(raw_stage<K>());
+        pend_a = base_a;
+        pend_b = base_b;
+        pend_lim_a = lim_a;
+        pend_lim_b = lim_b;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int win = r * NW + wave;
-            const int kk = dma_kk[r];
-            const bool hi = split && kk >= 16 * 41;
-            const char* src = (hi ? base_b : base_a) + (int64_t)min(kk, hi ? lim_b : lim_a) * 16;
-            lds_dma<16>(src, win < kWindows ? lds_addr(stage) + win * 1024 : lds_addr(s_junk));
-        }
+        for (int r = 0; r < (decltype(all)::value ? R : 1); ++r) copy_rows(r);
         advance(cl, p);
     };
 
@@ -616,7 +636,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
         // Every wave has read the raw stage of the unit it is dequantizing (conv_load, waited for
         // above): the next unit's copy can go there now, in the middle of the step, rather than with
         // every other wave's right after the step's opening barrier.
-        issue(kr2, ki4);
+        issue(kr2, ki4, std::integral_constant<bool, SPARSE>{});
         const int partner = wave < kHeadWaves ? wave + kHeadWaves : wave - kHeadWaves;
         const float* xq = s_xp[partner];
         float pq[4];
@@ -689,6 +709,11 @@ void decode_mla_kernel(MlaDecodeParams p) {
             const uint4 bop = bring[dt % kPre];
             if (dt + kPre < kDimTiles) bring[dt % kPre] = load_b(dt + kPre);
             O[dt] = mfma_k32<true>(Ag[dt / (kDimTiles / 2)], bop, O[dt]);
+            if constexpr (!SPARSE) {
+#pragma unroll
+                for (int r = 1; r < R; ++r)
+                    if (dt == (r * kDimTiles) / R) copy_rows(r);  // the rest of the next unit's copies
+            }
             if (dt % kTilesPerGroup == kTilesPerGroup - 1)
                 conv_store(kr2, kt2, vn, cin, (dt / kTilesPerGroup) * kConvPerGroup,
                            std::integral_constant<int, kConvPerGroup>{}, dt == kDimTiles - 1);
@@ -702,7 +727,6 @@ void decode_mla_kernel(MlaDecodeParams p) {
     auto step = [&](auto kst) __attribute__((always_inline)) -> bool {
         constexpr int K = decltype(kst)::value;
         constexpr int KR = K % 3, KT = K & 1, KR2 = (K + 1) % 3, KT2 = (K + 1) & 1;
-        prefetch_ids();
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * RL));  // own loads of unit u+1 are done
         compiler_fence();
         __builtin_amdgcn_s_barrier();                          // everyone's are; step u-1 is finished
@@ -715,6 +739,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
                 std::integral_constant<int, KT2>{}, nxt, std::integral_constant<int, (K + 4) % 6>{});
         if (__builtin_expect(cc.g + 1 == g_end || cc.k + 1 == cc.nu, 0)) end_segment();
         advance(cc, p);
+        prefetch_ids();
         return cc.g < g_end;
     };
 
@@ -727,11 +752,11 @@ void decode_mla_kernel(MlaDecodeParams p) {
         lds_barrier();
     }
     prefetch_ids();
-    issue(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    issue(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, std::true_type{});
     prefetch_ids();
-    issue(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+    issue(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, std::true_type{});
     prefetch_ids();
-    issue(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+    issue(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{}, std::true_type{});
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * RL));
     compiler_fence();
     __builtin_amdgcn_s_barrier();
@@ -745,7 +770,8 @@ void decode_mla_kernel(MlaDecodeParams p) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));  // own reads of raw stage 0 are done
     lds_barrier();                                     // everyone's are
     prefetch_ids();
-    issue(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
+    issue(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{}, std::true_type{});
+    prefetch_ids();
 
     while (true) {
         if (!step(std::integral_constant<int, 0>{})) break;

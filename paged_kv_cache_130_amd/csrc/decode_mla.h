@@ -40,9 +40,9 @@
 //    output registers are the PV A operand's token order (sigma of mfma_common.h, two 16-token tiles
 //    per k=32 step); the V operand comes from ds_read_b64_tr_b16, which transposes 4 x 4 blocks of
 //    16-bit values across the lanes of a 16-lane group.
-//  * Per unit: the opening barrier and the exchange barrier; the widening of unit u+1 and (dense
-//    form) all but the first of unit u+4's copy instructions are interleaved with the PV products
-//    of unit u, and operands are loaded four products ahead. The
+//  * Per unit: the opening barrier and the exchange barrier; the widening of unit u+1 and all but
+//    the first of unit u+4's copy instructions are interleaved with the PV products of unit u, and
+//    operands are loaded four products ahead. The
 //    softmax is online (lazy reference, as in the dense decode) and a segment that is not a whole
 //    sequence writes an fp32 partial merged by mla_merge_kernel (log-sum-exp).
 
@@ -315,24 +315,27 @@ void decode_mla_kernel(MlaDecodeParams p) {
 
     // The unit whose rows are being copied: its raw stage and where its rows come from (dense: the
     // block bases and last chunks of rows 0..15 and 16..31; sparse: its slot table and valid rows).
-    // Inside a step of the dense form only the first copy instruction goes out with the unit's issue;
-    // the other R - 1 are spread over the value products, so that the work-group's copies do not all
-    // queue at the address units at once (3% of the call). The sparse form issues them together: its
-    // copies read their slots from LDS, which inside the value products would wait for the prefetched
-    // value operands.
+    // Inside a step only the first copy instruction goes out with the unit's issue; the other R - 1
+    // are spread over the value products, so that the work-group's copies do not all queue at the
+    // address units at once (3% of the call). The sparse form reads the slots of all its copy
+    // instructions at issue (a read of LDS inside the value products would wait for the prefetched
+    // value operands), and spreads them only when there are at most three (eight waves); with fewer
+    // waves the copies go out together.
     uint32_t pend_stage = 0;
     const char* pend_a = dummy;
     const char* pend_b = dummy;
     int pend_lim_a = 0, pend_lim_b = 0;
     const int32_t* pend_tab = s_slot[0];
     int pend_v = 0;
+    int pend_sl[R];  // sparse, spread copies: the slot of each copy instruction's row, read at issue
+    constexpr bool kSpread = !SPARSE || R <= 3;
     auto copy_rows = [&](int r) __attribute__((always_inline)) {
         const int win = r * NW + wave;
         const int kk = dma_kk[r];
         const char* src;
         if constexpr (SPARSE) {
             const int row = kk / 41;  // >= 32 past the unit's last chunk
-            const int32_t sl = pend_tab[row & 31];
+            const int32_t sl = kSpread ? pend_sl[r] : pend_tab[row & 31];
             const bool ok = row < pend_v && (uint32_t)sl < (uint32_t)p.num_slots;
             src = ok ? p.kv + (int64_t)(sl >> p.block_size_log2) * p.block_stride +
                            (int64_t)(sl & (p.block_size - 1)) * kRow + (kk - row * 41) * 16
@@ -354,8 +357,12 @@ void decode_mla_kernel(MlaDecodeParams p) {
         pend_stage = lds_addr(raw_stage<K>());
         pend_tab = tab;
         pend_v = v;
+        if constexpr (kSpread) {
 #pragma unroll
-        for (int r = 0; r < (decltype(all)::value ? R : 1); ++r) copy_rows(r);
+            for (int r = 0; r < R; ++r) pend_sl[r] = tab[(dma_kk[r] / 41) & 31];
+        }
+#pragma unroll
+        for (int r = 0; r < (decltype(all)::value || !kSpread ? R : 1); ++r) copy_rows(r);
         copy_slot_table();
         advance(cl, p);
     };
@@ -636,7 +643,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
         // Every wave has read the raw stage of the unit it is dequantizing (conv_load, waited for
         // above): the next unit's copy can go there now, in the middle of the step, rather than with
         // every other wave's right after the step's opening barrier.
-        issue(kr2, ki4, std::integral_constant<bool, SPARSE>{});
+        issue(kr2, ki4, std::false_type{});
         const int partner = wave < kHeadWaves ? wave + kHeadWaves : wave - kHeadWaves;
         const float* xq = s_xp[partner];
         float pq[4];
@@ -709,7 +716,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
             const uint4 bop = bring[dt % kPre];
             if (dt + kPre < kDimTiles) bring[dt % kPre] = load_b(dt + kPre);
             O[dt] = mfma_k32<true>(Ag[dt / (kDimTiles / 2)], bop, O[dt]);
-            if constexpr (!SPARSE) {
+            if constexpr (kSpread) {
 #pragma unroll
                 for (int r = 1; r < R; ++r)
                     if (dt == (r * kDimTiles) / R) copy_rows(r);  // the rest of the next unit's copies

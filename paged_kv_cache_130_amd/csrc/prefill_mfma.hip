@@ -38,24 +38,34 @@ namespace {
 
 __device__ __forceinline__ int clamp_i(int v, int lo, int hi) { return max(lo, min(v, hi)); }
 
-// Query length of sequence s (0 for single-row sequences, which are decode rows).
-__device__ __forceinline__ int chunk_len(int s, const PrefillParams& p) {
-    const int ql = clamp_i(p.query_start_loc[s + 1] - p.query_start_loc[s], 0, p.max_query_len);
+// Query length from a sequence's query start and end (0 for single-row sequences, which are decode
+// rows).
+__device__ __forceinline__ int chunk_len(int qs, int qe, const PrefillParams& p) {
+    const int ql = clamp_i(qe - qs, 0, p.max_query_len);
     return ql >= 2 ? ql : 0;
 }
 
-__device__ __forceinline__ int row_blocks(int s, const PrefillParams& p) {
-    return (chunk_len(s, p) * p.group + p.rows_per_item - 1) / p.rows_per_item;
-}
+// The item of a work-group: its sequence, row block, the sequence's first query row, chunk length
+// and context length (as stored; clamped by the caller), all wave-uniform.
+struct ChunkItem {
+    int s, rb, q0, qlen, n;
+};
 
 // Work item w -> (sequence, row block), sequence-major, row blocks in descending order (the last row
-// blocks see the longest causal range, so the longest items are dispatched first).
-__device__ __forceinline__ bool find_chunk_work(int w, const PrefillParams& p, int& s_out, int& rb_out) {
+// blocks see the longest causal range, so the longest items are dispatched first). The query starts
+// and context lengths are read in the same pass, so the item's start waits for one round trip to
+// memory instead of two.
+__device__ __forceinline__ bool find_chunk_work(int w, const PrefillParams& p, ChunkItem& it) {
     const int lane = threadIdx.x & 63;
     int done = 0;
     for (int base = 0; base < p.num_seqs; base += 64) {
         const int s = base + lane;
-        const int n = s < p.num_seqs ? row_blocks(s, p) : 0;
+        const bool in = s < p.num_seqs;
+        const int qs = in ? p.query_start_loc[s] : 0;
+        const int qe = in ? p.query_start_loc[s + 1] : 0;
+        const int sl = in ? p.seq_lens[s] : 0;
+        const int ql = chunk_len(qs, qe, p);
+        const int n = (ql * p.group + p.rows_per_item - 1) / p.rows_per_item;
         int incl = n;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -68,8 +78,11 @@ __device__ __forceinline__ bool find_chunk_work(int w, const PrefillParams& p, i
             const int L = __builtin_ctzll(hit);
             const int before = done + __builtin_amdgcn_readlane(incl - n, L);
             const int cnt = __builtin_amdgcn_readlane(n, L);
-            s_out = base + L;
-            rb_out = cnt - 1 - (w - before);
+            it.s = base + L;
+            it.rb = cnt - 1 - (w - before);
+            it.q0 = __builtin_amdgcn_readlane(qs, L);
+            it.qlen = __builtin_amdgcn_readlane(ql, L);
+            it.n = __builtin_amdgcn_readlane(sl, L);
             return true;
         }
         done += total;
@@ -125,16 +138,15 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
     const int c = lane & 15;
 
     const int kvh = item % p.num_kv_heads;
-    int s, rb;
-    if (!find_chunk_work(item / p.num_kv_heads, p, s, rb)) return;  // the same for the whole work-group
+    ChunkItem itm;
+    if (!find_chunk_work(item / p.num_kv_heads, p, itm)) return;  // the same for the whole work-group
+    const int s = itm.s, rb = itm.rb, q0 = itm.q0, qlen = itm.qlen;
 
     const int G = p.group;
     const int bs = p.block_size;
     const int bs_log2 = p.tiles_per_block_log2 + 4;
-    const int q0 = __builtin_amdgcn_readfirstlane(p.query_start_loc[s]);
-    const int qlen = __builtin_amdgcn_readfirstlane(chunk_len(s, p));
     const int64_t ncap = min((int64_t)p.max_seq_len, (int64_t)p.bt_stride * bs);
-    const int n = (int)max((int64_t)0, min((int64_t)__builtin_amdgcn_readfirstlane(p.seq_lens[s]), ncap));
+    const int n = (int)max((int64_t)0, min((int64_t)itm.n, ncap));
     const int R = qlen * G;                                 // rows of this K/V head in this chunk
     const int wg_r0 = rb * kPRows;
     const int wg_rend = min(R, wg_r0 + kPRows);
@@ -484,33 +496,49 @@ __device__ __forceinline__ void prefill_block(const PrefillParams& p, const int 
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     lds_barrier();
-    if (grp == 1) return;
 
+    // Group 0 merges its rows with group 1's and puts them, in the output type, into a row-major
+    // staging tile [128 rows x 128 dims] (the second V stage, free by now); then all 8 waves write
+    // the tile's rows out as 16-byte stores.
+    char* stg = s_pv1;
+    if (grp == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            // Weights of the two halves for row 16 nt + c: 2^(m_i - M) with M the larger reference (a
+            // half without visible tokens has m = -inf and weight 0).
+            const float m1 = xm[2 * (16 * nt + c)];
+            const float l1 = xm[2 * (16 * nt + c) + 1];
+            const float M = fmaxf(m[nt], m1);
+            const float w0 = m[nt] == M ? 1.f : fast_exp2(m[nt] - M);
+            const float w1 = m1 == M ? 1.f : fast_exp2(m1 - M);
+            const float Lc = w0 * lt[nt] + w1 * l1;
+            const float inv_c = Lc > 0.f ? 1.f / Lc : 0.f;  // no visible token (inconsistent lengths): output 0
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int rl = 32 * wv + 16 * nt + 4 * g4 + jj;  // row within the work-group
+                const float a0 = __shfl(w0 * inv_c, 4 * g4 + jj);
+                const float a1 = __shfl(w1 * inv_c, 4 * g4 + jj);
+                const float* x1 = xo + (16 * nt + 4 * g4 + jj) * kD + c;
+                uint16_t* st = reinterpret_cast<uint16_t*>(stg + rl * kPRow) + c;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+                    st[16 * dt] = (uint16_t)(pack2<BF16>(fmaf(O[nt][dt][jj], a0, x1[16 * dt] * a1), 0.f) & 0xFFFFu);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    lds_barrier();
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        // Weights of the two halves for row 16 nt + c: 2^(m_i - M) with M the larger reference (a
-        // half without visible tokens has m = -inf and weight 0).
-        const float m1 = xm[2 * (16 * nt + c)];
-        const float l1 = xm[2 * (16 * nt + c) + 1];
-        const float M = fmaxf(m[nt], m1);
-        const float w0 = m[nt] == M ? 1.f : fast_exp2(m[nt] - M);
-        const float w1 = m1 == M ? 1.f : fast_exp2(m1 - M);
-        const float Lc = w0 * lt[nt] + w1 * l1;
-        const float inv_c = Lc > 0.f ? 1.f / Lc : 0.f;  // no visible token (inconsistent lengths): output 0
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int r = r0 + 16 * nt + 4 * g4 + jj;
-            const float a0 = __shfl(w0 * inv_c, 4 * g4 + jj);
-            const float a1 = __shfl(w1 * inv_c, 4 * g4 + jj);
-            if (r >= rend) continue;
+    for (int k = 0; k < kPRows * 16 / (64 * kPWaves); ++k) {
+        const int t = threadIdx.x + 64 * kPWaves * k;
+        const int rl = t >> 4, ch = t & 15;
+        const int r = wg_r0 + rl;
+        if (r < wg_rend) {
             const int pos = r / G;
             const int head = r - pos * G;
-            uint16_t* o = out + ((size_t)(q0 + pos) * p.num_q_heads + hq0 + head) * kD + c;
-            const float* x1 = xo + (16 * nt + 4 * g4 + jj) * kD + c;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                o[16 * dt] = (uint16_t)(pack2<BF16>(fmaf(O[nt][dt][jj], a0, x1[16 * dt] * a1), 0.f) & 0xFFFFu);
+            *reinterpret_cast<uint4*>(out + ((size_t)(q0 + pos) * p.num_q_heads + hq0 + head) * kD + 8 * ch) =
+                *reinterpret_cast<const uint4*>(stg + rl * kPRow + 16 * ch);
         }
     }
 }

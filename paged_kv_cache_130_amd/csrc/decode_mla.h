@@ -574,9 +574,9 @@ void decode_mla_kernel(MlaDecodeParams p) {
 
         // Scores of this wave's own 16-token tile (t = half): 18 A operands, loaded kPre products
         // ahead. Order: the two RoPE k-steps (16, 17) into S, then the latent k-steps group by group
-        // (g = 0..3: k-steps 4g .. 4g+3) into Sg[0] / Sg[1] (two accumulator chains, even and odd
-        // k-steps); once a group's last product is issued, its sums are scaled per row and added to
-        // S. Register j holds token 16 half + g4 + 4j of head column c.
+        // (g = 0..3: k-steps 4g .. 4g+3) into Sg[g & 1] (one accumulator per group, alternating, so
+        // that a group's products run while the previous group's sums are scaled per row and added
+        // to S). Register j holds token 16 half + g4 + 4j of head column c.
         constexpr int kPre = 4;
         constexpr int kA = kKSteps;
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -601,12 +601,12 @@ void decode_mla_kernel(MlaDecodeParams p) {
             } else {
                 const int y = x - 2, g = y >> 2, kk = y & 3;
                 if (kk == 0) sg = *reinterpret_cast<const float4*>(scl + 32 * g + 4 * half);
-                Sg[kk & 1] = mfma_k32<true>(a, qr[ks_of(x)], kk < 2 ? zero : Sg[kk & 1]);
+                Sg[g & 1] = mfma_k32<true>(a, qr[ks_of(x)], kk == 0 ? zero : Sg[g & 1]);
                 if (kk == 3) {
-                    S[0] = fmaf(sg.x, Sg[0][0] + Sg[1][0], S[0]);
-                    S[1] = fmaf(sg.y, Sg[0][1] + Sg[1][1], S[1]);
-                    S[2] = fmaf(sg.z, Sg[0][2] + Sg[1][2], S[2]);
-                    S[3] = fmaf(sg.w, Sg[0][3] + Sg[1][3], S[3]);
+                    S[0] = fmaf(sg.x, Sg[g & 1][0], S[0]);
+                    S[1] = fmaf(sg.y, Sg[g & 1][1], S[1]);
+                    S[2] = fmaf(sg.z, Sg[g & 1][2], S[2]);
+                    S[3] = fmaf(sg.w, Sg[g & 1][3], S[3]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -620,8 +620,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
         float mx = kNegInf;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) mx = ok[jj] ? fmaxf(mx, S[jj]) : mx;
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = row_max4(mx);
         // This tile's probabilities against the wave's own reference: the running reference m, moved
         // to the tile maximum if that exceeds it by more than kRescaleSlack (so p <= 2^kRescaleSlack).
         const float tmax = mx * sl2;

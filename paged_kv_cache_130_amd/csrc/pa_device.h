@@ -47,6 +47,19 @@ __device__ __forceinline__ int wave_sum_int(int x) {
     return x;
 }
 
+// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (one position in each 16-lane row), every lane
+// of the four getting it. gfx950's row swaps do it on the VALU without an LDS round trip: with both
+// operands x, v_permlane16_swap returns rows (0, 0, 2, 2) of x in one result and rows (1, 1, 3, 3)
+// in the other, and v_permlane32_swap returns halves (0, 0) and (1, 1).
+__device__ __forceinline__ float row_max4(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 2-element dot product with fp32 accumulation (v_dot2_f32_f16 / v_dot2_f32_bf16).

@@ -69,6 +69,20 @@ __device__ __forceinline__ void lds_dma(const void* src, uint32_t lds) {
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory");
 }
 
+// The same copy from a wave-uniform base plus a per-lane 32-bit byte offset (the instruction's
+// scalar-base form: no 64-bit address arithmetic per lane).
+template <int BYTES>
+__device__ __forceinline__ void lds_dma_sv(const void* base, uint32_t off, uint32_t lds) {
+    static_assert(BYTES == 16, "16 bytes per lane");
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    // readfirstlane returns int: both halves are zero-extended through uint32_t.
+    const uint64_t sb = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(m0)
+                 : "memory");
+}
+
 // Two E4M3 codes (bytes 0, 1 of w, or bytes 2, 3 when HI) -> two bf16 in one dword, the first in the
 // low half. Exact: every E4M3 value is a bf16 value, and the scale is 1.
 template <bool HI>

@@ -341,7 +341,12 @@ void decode_mla_kernel(MlaDecodeParams p) {
                            (int64_t)(sl & (p.block_size - 1)) * kRow + (kk - row * 41) * 16
                      : dummy;
         } else {
-            const bool hi = p.block_size < kUnit && kk >= 16 * 41;
+            if (p.block_size >= kUnit) {  // one block holds the unit: one base for all rows
+                lds_dma_sv<16>(pend_a, (uint32_t)min(kk, pend_lim_a) * 16u,
+                               win < kWindows ? pend_stage + win * 1024 : lds_addr(s_junk));
+                return;
+            }
+            const bool hi = kk >= 16 * 41;
             src = (hi ? pend_b : pend_a) + (int64_t)min(kk, hi ? pend_lim_b : pend_lim_a) * 16;
         }
         lds_dma<16>(src, win < kWindows ? pend_stage + win * 1024 : lds_addr(s_junk));
@@ -418,9 +423,10 @@ void decode_mla_kernel(MlaDecodeParams p) {
     };
 
     // Dequantization of a unit: raw stage KR (validity vi) -> tile stage KT. Item it is row
-    // it * NW + wave (the same for the whole wave), 8 bytes per lane; rows past the valid ones write
-    // zeros (their stale LDS bytes are read but not used). conv_load issues the LDS reads of all
-    // items; conv_store converts and writes items [i0, i0 + CNT) and, if rope, the RoPE chunks.
+    // it * NW + wave (the same for the whole wave), 8 bytes per lane; rows past the valid ones are
+    // not written (their stale raw bytes are read but not used) and get a zero scale. conv_load
+    // issues the LDS reads of all items; conv_store converts and writes items [i0, i0 + CNT) and, if
+    // rope, the RoPE chunks and the scales.
     struct ConvIn {
         uint2 b8[kLatentIters];
         uint4 rope[kRopeIters];
@@ -453,10 +459,10 @@ void decode_mla_kernel(MlaDecodeParams p) {
             const int it = i0 + jj;
             if (it < kLatentIters) {
                 const int r = it * NW + wave;  // wave-uniform
-                const uint4 d = codes8(in.b8[it]);
-                const bool keep = (vmask >> r) & 1u;
-                *reinterpret_cast<uint4*>(tile + r * kTileRow + ((lane ^ swz(r)) << 4)) =
-                    keep ? d : make_uint4(0u, 0u, 0u, 0u);
+                // A row without a token keeps what the stage held (finite: zeros from the prologue or
+                // an earlier token's values), so that its zero probability meets no NaN.
+                if ((vmask >> r) & 1u)
+                    *reinterpret_cast<uint4*>(tile + r * kTileRow + ((lane ^ swz(r)) << 4)) = codes8(in.b8[it]);
             }
         }
         if (rope) {
@@ -465,10 +471,8 @@ void decode_mla_kernel(MlaDecodeParams p) {
                 const int n = it * 64 * NW + tid;
                 if (kRopeChunks % (64 * NW) == 0 || n < kRopeChunks) {
                     const int r = n >> 3, k8 = n & 7;
-                    const uint4 d = in.rope[it];
-                    const bool keep = (vmask >> r) & 1u;
-                    *reinterpret_cast<uint4*>(tile + r * kTileRow + ((64 + (k8 ^ swz(r))) << 4)) =
-                        keep ? d : make_uint4(0u, 0u, 0u, 0u);
+                    // RoPE values enter only the scores, which are masked for rows without a token.
+                    *reinterpret_cast<uint4*>(tile + r * kTileRow + ((64 + (k8 ^ swz(r))) << 4)) = in.rope[it];
                 }
             }
             // The unit's scales into the table of tile stage KT (0 for rows without a token).
@@ -759,6 +763,10 @@ void decode_mla_kernel(MlaDecodeParams p) {
     }
     prefetch_ids();
     issue(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, std::true_type{});
+    // Both tile stages start as zeros (finite values for the rows the dequantization skips).
+    for (int i = tid; i < 2 * kTileStage / 16; i += 64 * NW)
+        *reinterpret_cast<uint4*>((i < kTileStage / 16 ? s_tile0 : s_tile1) + 16 * (i % (kTileStage / 16))) =
+            make_uint4(0u, 0u, 0u, 0u);
     prefetch_ids();
     issue(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, std::true_type{});
     prefetch_ids();

@@ -183,7 +183,8 @@ bool mla_layout(const pa_attn_desc& d, int32_t num_seqs, int32_t max_context_len
 }
 
 size_t mla_decode_ws(const MlaLayout& L, int32_t num_q_heads, int32_t num_seqs) {
-    return (size_t)L.slots * num_q_heads * (512 + 2) * sizeof(float) + (size_t)num_seqs * 2 * sizeof(int32_t);
+    return (size_t)L.slots * num_q_heads * (512 * sizeof(uint16_t) + 2 * sizeof(float)) +
+           (size_t)num_seqs * 2 * sizeof(int32_t);
 }
 
 // Device address of `scratch` on the device that runs `stream`, resolved once per device (with that
@@ -259,9 +260,10 @@ int32_t mla_decode_call(void* out, const void* q, const void* k_cache, const int
     p.kv = static_cast<const char*>(k_cache) + d.k_view.offset + (int64_t)d.layer * d.k_view.layer_stride;
     p.block_tables = block_tables;
     p.context_lens = lens;
-    float* ws = static_cast<float*>(workspace);
-    p.part_acc = ws;
-    p.part_ml = ws + L.slots * d.num_q_heads * 512;
+    // Workspace: bf16 partial outputs [slots, Hq, 512], then fp32 (m, l) [slots, Hq, 2], then the
+    // sequences' first and last work-groups.
+    p.part_acc = static_cast<uint16_t*>(workspace);
+    p.part_ml = reinterpret_cast<float*>(p.part_acc + L.slots * d.num_q_heads * 512);
     p.seq_meta = reinterpret_cast<int32_t*>(p.part_ml + L.slots * d.num_q_heads * 2);
     p.block_stride = d.k_view.block_stride;
     p.num_blocks = d.num_blocks;

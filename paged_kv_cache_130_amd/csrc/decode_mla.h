@@ -531,32 +531,24 @@ void decode_mla_kernel(MlaDecodeParams p) {
             Mr[j] = __shfl(m, 4 * g4 + j);
         }
         const size_t row0 = (size_t)cc.s * Hq + head0 + 4 * g4;  // head row of register 0
-        if (whole) {
-            float inv[4];
+        // A whole sequence writes its output; a segment of one writes its own normalised output
+        // O / L in bf16 (to slot s + w) and its (m, L), which mla_merge_kernel weighs.
+        const size_t idx0 = row0 + (size_t)w * Hq;  // slot s + w
+        uint16_t* o = whole ? reinterpret_cast<uint16_t*>(p.out) + row0 * 512 + c : p.part_acc + idx0 * 512 + c;
+        float inv[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) inv[j] = Lr[j] > 0.f ? 1.f / Lr[j] : 0.f;
-            uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row0 * 512 + c;
+        for (int j = 0; j < 4; ++j) inv[j] = Lr[j] > 0.f ? 1.f / Lr[j] : 0.f;
 #pragma unroll
-            for (int dt = 0; dt < kDimTiles; ++dt) {
+        for (int dt = 0; dt < kDimTiles; ++dt) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    o[j * 512 + 16 * (dt0 + dt)] = (uint16_t)(pack2<true>(O[dt][j] * inv[j], 0.f) & 0xFFFFu);
-                __builtin_amdgcn_sched_barrier(0);  // one tile at a time (see the rescale)
-            }
-        } else {
-            const size_t idx0 = row0 + (size_t)w * Hq;  // slot s + w
-            float* a = p.part_acc + idx0 * 512 + c;
+            for (int j = 0; j < 4; ++j)
+                o[j * 512 + 16 * (dt0 + dt)] = (uint16_t)(pack2<true>(O[dt][j] * inv[j], 0.f) & 0xFFFFu);
+            __builtin_amdgcn_sched_barrier(0);  // one tile at a time (see the rescale)
+        }
+        if (!whole && c == 0 && half == 0) {
 #pragma unroll
-            for (int dt = 0; dt < kDimTiles; ++dt) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) a[j * 512 + 16 * (dt0 + dt)] = O[dt][j];
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (c == 0 && half == 0) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<float2*>(p.part_ml + (idx0 + j) * 2) = make_float2(Mr[j], Lr[j]);
-            }
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<float2*>(p.part_ml + (idx0 + j) * 2) = make_float2(Mr[j], Lr[j]);
         }
     };
 

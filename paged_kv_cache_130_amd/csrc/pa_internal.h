@@ -127,7 +127,7 @@ struct MlaDecodeParams {
     const int32_t* block_tables;
     const int32_t* context_lens;
     float* part_ml;            // [slots, Hq, 2]: reference max (log2 domain), sum
-    float* part_acc;           // [slots, Hq, 512]: unnormalised accumulator
+    uint16_t* part_acc;        // [slots, Hq, 512]: the partial's output O / l, bf16
     int32_t* seq_meta;         // [num_seqs, 2]: first and last work-group of the sequence
     int64_t block_stride;
     int64_t num_blocks;

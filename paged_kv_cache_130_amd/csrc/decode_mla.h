@@ -44,7 +44,8 @@
 //    the first of unit u+4's copy instructions are interleaved with the PV products of unit u, and
 //    operands are loaded four products ahead. The
 //    softmax is online (lazy reference, as in the dense decode) and a segment that is not a whole
-//    sequence writes an fp32 partial merged by mla_merge_kernel (log-sum-exp).
+//    sequence writes its own output O / l in bf16 and its (m, l), which mla_merge_kernel weighs
+//    (log-sum-exp).
 
 #pragma once
 

@@ -425,7 +425,7 @@ void decode_mla_kernel(MlaDecodeParams p) {
 
     // Dequantization of a unit: raw stage KR (validity vi) -> tile stage KT. Item it is row
     // it * NW + wave (the same for the whole wave), 8 bytes per lane; rows past the valid ones are
-    // not written (their stale raw bytes are read but not used) and get a zero scale. conv_load
+    // written as zeros (their stale raw bytes are read but not used) and get a zero scale. conv_load
     // issues the LDS reads of all items; conv_store converts and writes items [i0, i0 + CNT) and, if
     // rope, the RoPE chunks and the scales.
     struct ConvIn {
@@ -460,10 +460,11 @@ void decode_mla_kernel(MlaDecodeParams p) {
             const int it = i0 + jj;
             if (it < kLatentIters) {
                 const int r = it * NW + wave;  // wave-uniform
-                // A row without a token keeps what the stage held (finite: zeros from the prologue or
-                // an earlier token's values), so that its zero probability meets no NaN.
-                if ((vmask >> r) & 1u)
-                    *reinterpret_cast<uint4*>(tile + r * kTileRow + ((lane ^ swz(r)) << 4)) = codes8(in.b8[it]);
+                // A row without a token is written as zeros (its codes are cleared before they are
+                // widened), so that its zero probability meets no NaN from stale bytes.
+                const bool keep = (vmask >> r) & 1u;
+                *reinterpret_cast<uint4*>(tile + r * kTileRow + ((lane ^ swz(r)) << 4)) =
+                    codes8(keep ? in.b8[it] : make_uint2(0u, 0u));
             }
         }
         if (rope) {
@@ -756,10 +757,6 @@ void decode_mla_kernel(MlaDecodeParams p) {
     }
     prefetch_ids();
     issue(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, std::true_type{});
-    // Both tile stages start as zeros (finite values for the rows the dequantization skips).
-    for (int i = tid; i < 2 * kTileStage / 16; i += 64 * NW)
-        *reinterpret_cast<uint4*>((i < kTileStage / 16 ? s_tile0 : s_tile1) + 16 * (i % (kTileStage / 16))) =
-            make_uint4(0u, 0u, 0u, 0u);
     prefetch_ids();
     issue(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, std::true_type{});
     prefetch_ids();

@@ -180,3 +180,31 @@ def test_full_size_dsa_mla_sampled():
                     q_norope[..., 512:] = 0
                     ref_nr = A.mla_decode(q_norope, sub, mla_v, layer, tbl, [n], BS, case.scale)
                     assert_discriminating(ref[0], ref_nr[0], what)
+
+
+def test_nan_row_stays_in_its_sequence():
+    """NaN codes in one sequence's valid row reach no other sequence's output.
+
+    One work-group range covers all units (partition_size 1024), so later units reuse the tile rows
+    of the unit with the NaN; the rows without a token in those units must not carry it into the
+    value product (a zero probability times NaN is NaN)."""
+    ctx = [40, 5, 70, 33]
+    need = sum(P.blocks_needed(n, BS) for n in ctx)
+    case = workloads.make_mla_case(seed=991, context_lens=ctx, num_blocks=need + 1, num_q_heads=64)
+    img, host = populate(case)
+    mla_v, _, _ = views()
+    nan_codes = np.full(16, 0x7F, dtype=np.uint8)  # e4m3 NaN
+    for layer in range(2):
+        blk = int(case.block_tables[0, 0])
+        a = P.address(mla_v, layer, blk, 20)  # sequence 0, token 20: latent bytes 0..15
+        host[a:a + 16] = nan_codes
+    img.view(-1)[:] = torch.from_numpy(host).to("cuda")
+    for layer in range(2):
+        out = mla_decode_gpu(case, img, layer, partition_size=1024)
+        got = out.view(torch.bfloat16).double().cpu().numpy()
+        assert not np.isfinite(got[0]).all(), "the NaN row should reach its own sequence"
+        ref = A.mla_decode(bits_np(case.q), host, mla_v, layer, case.block_tables, case.context_lens, BS,
+                           case.scale)
+        for s in range(1, len(ctx)):
+            assert np.isfinite(got[s]).all(), f"layer {layer} seq {s}: NaN from another sequence"
+            assert_close(got[s], ref[s], MLA_ATOL, MLA_RTOL, f"layer {layer} seq {s}")

@@ -650,7 +650,7 @@ def rounded(x):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs on a single MI355X (no multi-GPU path). "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (one MI355X). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch

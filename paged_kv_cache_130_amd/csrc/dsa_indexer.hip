@@ -190,12 +190,17 @@ __device__ __forceinline__ void lds_sync() {
     lds_barrier();
 }
 
+// Inclusive prefix sum over the 64 lanes, on the VALU through DPP: shifts by 1, 2, 4 and 8 lanes
+// within each 16-lane row, then lane 15 of each row added to the next row and lane 31 to rows 2 and
+// 3 (row_bcast:15 and row_bcast:31). A lane without a source adds 0.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl(v, max(lane - off, 0));
-        if (lane >= off) v += t;
-    }
+    (void)lane;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
     return v;
 }
 

@@ -147,3 +147,28 @@ def test_full_size_13b_shape_fp8_sampled():
     rng = np.random.default_rng(3)
     select = [(int(b), int(h)) for b, h in zip(rng.integers(0, case.num_seqs, 12), rng.integers(0, 40, 12))]
     decode(case, k8, v8, 0, select=select)
+
+
+def test_full_size_gqa_copied_prefix_fp8_sampled():
+    # The GQA-8 batch (256 sequences, a 2000-token prompt copied into each sequence's own blocks plus
+    # lognormal suffixes, 32/8 heads of 128, bf16) with its K/V quantized to FP8: the matrix-core FP8
+    # decode at the bench's full size and library-chosen partitions; sampled (sequence, head) outputs.
+    case = workloads.make_dense_case("gqa_prefix", device="cuda", copied_prefix=True)
+    assert case.dtype == "bf16"
+    nb, bs, hkv, d = case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim
+    view = pa.dense_view(bs, hkv, d, 1)
+    k8 = torch.empty((nb, bs, hkv, d), dtype=torch.uint8, device="cuda")
+    v8 = torch.empty_like(k8)
+    slots = torch.arange(nb * bs, dtype=torch.int64, device="cuda")
+    ksrc = torch.nan_to_num(case.k_pool.view(torch.bfloat16), nan=0.0).reshape(nb * bs, hkv * d)
+    vsrc = torch.nan_to_num(case.v_pool.view(torch.bfloat16), nan=0.0).reshape(nb * bs, hkv * d)
+    pa.pa_quantize_and_cache(ksrc, slots, k8, view, 0, bs, nb, K_SCALE, v=vsrc, v_cache=v8, v_view=view,
+                             v_scale=V_SCALE)
+    torch.cuda.synchronize()
+    del ksrc, vsrc
+    case.k_pool = case.v_pool = None
+    rng = np.random.default_rng(4)
+    select = [(int(b), int(h)) for b, h in zip(rng.integers(0, case.num_seqs, 12),
+                                               rng.integers(0, case.num_q_heads, 12))]
+    select.append((int(np.argmax(case.context_lens)), case.num_q_heads - 1))
+    decode(case, k8, v8, 0, select=select)

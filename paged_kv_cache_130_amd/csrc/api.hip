@@ -92,6 +92,12 @@ int32_t effective_partition(const pa_attn_desc& d, int32_t num_seqs, int32_t max
     return whole_blocks(256);
 }
 
+// Wave items per stored K/V head in the vector decode kernels: eight query heads per K/V head at
+// head_dim 64 or 256 take two waves of four (decode_dense.hip, decode_fp8.hip).
+int64_t kv_waves(const pa_attn_desc& d) {
+    return (d.qk_dim != 128 && d.num_q_heads == 8 * d.num_kv_heads) ? 2 : 1;
+}
+
 int32_t check_dense_desc(const pa_attn_desc& d) {
     if (d.kv_format != PA_KV_F16 && d.kv_format != PA_KV_BF16 && d.kv_format != PA_KV_FP8_E4M3)
         return PA_ERR_UNSUPPORTED;
@@ -526,7 +532,7 @@ int32_t decode_entry(void* out, const void* q, const void* k_cache, const void* 
     const int32_t P = effective_partition(d, num_seqs, max_context_len);
     const int64_t max_parts64 = ((int64_t)max_context_len + P - 1) / P;
     const int32_t max_parts = max_parts64 < 1 ? 1 : (int32_t)max_parts64;
-    if ((int64_t)d.num_kv_heads * num_seqs * max_parts > 0x7FFFFFFFLL - 64) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)d.num_kv_heads * kv_waves(d) * num_seqs * max_parts > 0x7FFFFFFFLL - 64) return PA_ERR_UNSUPPORTED;
     const size_t need = dense_decode_ws(d, num_seqs, max_context_len);
     st = take_workspace(need, no_alloc, stream, workspace, workspace_bytes);
     if (st != PA_OK) return st;
@@ -621,7 +627,7 @@ int32_t pa_prefill_chunk(void* out, const void* q, const void* k_cache, const vo
     const int32_t P = effective_partition(d, num_seqs, max_seq_len);
     const int64_t max_parts64 = ((int64_t)max_seq_len + P - 1) / P;
     const int32_t max_parts = max_parts64 < 1 ? 1 : (int32_t)max_parts64;
-    if ((int64_t)d.num_kv_heads * num_seqs * max_parts > 0x7FFFFFFFLL - 64) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)d.num_kv_heads * kv_waves(d) * num_seqs * max_parts > 0x7FFFFFFFLL - 64) return PA_ERR_UNSUPPORTED;
     if ((int64_t)total_q * d.num_q_heads > 0x7FFFFFFFLL / 2) return PA_ERR_UNSUPPORTED;
 
     const char* kb = static_cast<const char*>(k_cache) + d.k_view.offset + (int64_t)d.layer * d.k_view.layer_stride;

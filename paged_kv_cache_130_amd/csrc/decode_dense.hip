@@ -196,8 +196,9 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
     // Per-lane byte offset inside a tile (32-bit) and the uniform per-tile base (64-bit): loads take the
     // scalar-base + vector-offset form.
     const int64_t krow = p.k_row_bytes, vrow = p.v_row_bytes;
-    const uint32_t klane = (uint32_t)(kvh * (D * 2) + c * 16) + (uint32_t)r * (uint32_t)krow;
-    const uint32_t vlane = (uint32_t)(kvh * (D * 2) + c * 16) + (uint32_t)r * (uint32_t)vrow;
+    const int kvs = kvh >> p.kv_shift;  // the stored K/V head
+    const uint32_t klane = (uint32_t)(kvs * (D * 2) + c * 16) + (uint32_t)r * (uint32_t)krow;
+    const uint32_t vlane = (uint32_t)(kvs * (D * 2) + c * 16) + (uint32_t)r * (uint32_t)vrow;
     const uint32_t nb = (uint32_t)p.num_blocks;
     const int tpb_log2 = p.tiles_per_block_log2;  // block_size / 16 is a power of two
     const int tpb_mask = (1 << tpb_log2) - 1;
@@ -328,13 +329,23 @@ hipError_t launch_typed(const DenseDecodeParams& p, hipStream_t stream) {
     return launch_decode_reduce(p, stream);
 }
 
+// Eight query heads per K/V head: two waves of four each read the K/V head (an eight-head wave
+// would need more than its 512 registers). The host counts these items (kv_waves in api.hip).
+inline DenseDecodeParams split_eight(const DenseDecodeParams& p) {
+    DenseDecodeParams q = p;
+    q.num_kv_heads = p.num_kv_heads * 2;
+    q.group = 4;
+    q.kv_shift = 1;
+    return q;
+}
+
 template <bool BF16, int D>
 hipError_t launch_group(const DenseDecodeParams& p, hipStream_t stream) {
     switch (p.group) {
         case 1: return launch_typed<BF16, D, 1>(p, stream);
         case 2: return launch_typed<BF16, D, 2>(p, stream);
         case 4: return launch_typed<BF16, D, 4>(p, stream);
-        case 8: return launch_typed<BF16, D, 8>(p, stream);
+        case 8: return launch_typed<BF16, D, 4>(split_eight(p), stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -343,7 +354,8 @@ template <bool BF16>
 hipError_t launch_dim(const DenseDecodeParams& p, hipStream_t stream) {
     switch (p.head_dim) {
         case 64: return launch_group<BF16, 64>(p, stream);
-        case 128: return launch_group<BF16, 128>(p, stream);
+        // Grouped heads at head_dim 128 run on the matrix cores (launch_decode_dense).
+        case 128: return p.group == 1 ? launch_typed<BF16, 128, 1>(p, stream) : hipErrorInvalidValue;
         case 256: return launch_group<BF16, 256>(p, stream);
         default: return hipErrorInvalidValue;
     }

@@ -178,8 +178,9 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(DenseDecodeParams p) {
     const int tbl = lane < nblk ? bt[lb0 + lane] : 0;
 
     const int64_t krow = p.k_row_bytes, vrow = p.v_row_bytes;
-    const uint32_t klane = (uint32_t)(kvh * D + c * 16) + (uint32_t)r * (uint32_t)krow;
-    const uint32_t vlane = (uint32_t)(kvh * D + c * 16) + (uint32_t)r * (uint32_t)vrow;
+    const int kvs = kvh >> p.kv_shift;  // the stored K/V head
+    const uint32_t klane = (uint32_t)(kvs * D + c * 16) + (uint32_t)r * (uint32_t)krow;
+    const uint32_t vlane = (uint32_t)(kvs * D + c * 16) + (uint32_t)r * (uint32_t)vrow;
     const uint32_t nb = (uint32_t)p.num_blocks;
     const int tpb_log2 = p.tiles_per_block_log2;
     const int tpb_mask = (1 << tpb_log2) - 1;
@@ -295,7 +296,15 @@ hipError_t launch_f8_group(const DenseDecodeParams& p, hipStream_t stream) {
         case 1: return launch_f8<D, 1>(p, stream);
         case 2: return launch_f8<D, 2>(p, stream);
         case 4: return launch_f8<D, 4>(p, stream);
-        case 8: return launch_f8<D, 8>(p, stream);
+        case 8: {
+            // Two waves of four query heads each per K/V head (an eight-head wave would need more
+            // than its 512 registers); the host counts these items (kv_waves in api.hip).
+            DenseDecodeParams q = p;
+            q.num_kv_heads = p.num_kv_heads * 2;
+            q.group = 4;
+            q.kv_shift = 1;
+            return launch_f8<D, 4>(q, stream);
+        }
         default: return hipErrorInvalidValue;
     }
 }
@@ -306,7 +315,8 @@ hipError_t launch_decode_fp8(const DenseDecodeParams& p, hipStream_t stream) {
     if (p.num_seqs <= 0) return hipSuccess;
     switch (p.head_dim) {
         case 64: return launch_f8_group<64>(p, stream);
-        case 128: return launch_f8_group<128>(p, stream);
+        // Grouped heads at head_dim 128 run on the matrix cores (launch_decode_dense).
+        case 128: return p.group == 1 ? launch_f8<128, 1>(p, stream) : hipErrorInvalidValue;
         case 256: return launch_f8_group<256>(p, stream);
         default: return hipErrorInvalidValue;
     }

@@ -101,7 +101,9 @@ struct DenseDecodeParams {
     float scale_log2;          // softmax scale * log2(e)
     int32_t is_bf16;
     int32_t head_dim;
-    int32_t group;             // Hq / Hkv
+    int32_t group;             // query heads per wave item (Hq / Hkv, or 4 when kv_shift is 1)
+    int32_t kv_shift;          // item K/V head >> kv_shift = stored K/V head (1: two waves of four
+                               // query heads share each stored head; num_kv_heads counts the items)
     int32_t kv_fp8;            // 1: E4M3 rows (one byte per value), bf16 queries and outputs
     float v_scale;             // FP8 rows: V value = code * v_scale (K's scale is folded into scale_log2)
 };

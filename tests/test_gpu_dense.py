@@ -94,6 +94,12 @@ SHAPES = [
     ("bf16", 8, 2, 128, 16, [1100, 2100, 3, 0], 16),
     ("f16", 4, 4, 128, 16, [1300, 2, 1025], 16),
     ("bf16", 4, 4, 256, 16, [1040, 17], 16),
+    # head_dim 64 and 256 with four and eight query heads per K/V head (eight: two waves of four
+    # read each K/V head)
+    ("bf16", 32, 8, 64, 16, [3, 100, 900], 0),
+    ("f16", 64, 8, 64, 16, [2, 70, 1200], 128),
+    ("bf16", 16, 4, 256, 16, [5, 300, 800], 0),
+    ("f16", 16, 2, 256, 32, [9, 200, 1100], 256),
 ]
 
 

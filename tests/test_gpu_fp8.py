@@ -92,6 +92,11 @@ SHAPES = [
     (24, 8, 128, 16, [2, 3, 4, 5, 33], 0),    # group 3, matrix cores, short rows
     (8, 2, 128, 16, [1100, 2100, 1, 0], 16),  # more than 64 and 128 partials per row, matrix cores
     (4, 4, 128, 16, [1300, 3, 1025], 16),     # more than 64 partials, vector kernel
+    # head_dim 64 and 256, four and eight query heads per K/V head (eight: two waves of four each)
+    (32, 8, 64, 16, [3, 100, 900], 0),
+    (16, 2, 64, 16, [2, 70, 1200], 128),
+    (16, 4, 256, 16, [5, 300, 800], 0),
+    (16, 2, 256, 32, [9, 200, 1100], 64),
 ]
 
 

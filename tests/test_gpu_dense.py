@@ -111,6 +111,29 @@ def test_decode_shapes(dtype, Hq, Hkv, D, bs, ctx, part):
     run_case(case, part)
 
 
+# partition_size far above every context (2^20 tokens). The library uses at most 64 blocks per
+# partition: at block size 256 every context here (up to 16,384 tokens) is one partition, so no
+# workspace and no merge; at block size 16 the long contexts are cut at 1,024 tokens.
+UNBOUNDED = [
+    # dtype, Hq, Hkv, bs, contexts, single partition
+    ("f16", 4, 4, 256, [16000, 5, 257, 9000], True),    # vector kernel
+    ("bf16", 8, 2, 256, [12000, 700, 1], True),         # matrix-core kernel
+    ("bf16", 8, 8, 16, [3000, 40], False),
+]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,bs,ctx,single", UNBOUNDED)
+def test_partition_beyond_every_context(dtype, Hq, Hkv, bs, ctx, single):
+    need = sum(P.blocks_needed(n, bs) for n in ctx)
+    case = workloads.make_dense_case("tiny", seed=4500 + Hq + bs, context_lens=ctx, num_blocks=need + 3,
+                                     num_q_heads=Hq, num_kv_heads=Hkv, block_size=bs, dtype=dtype)
+    part = 1 << 20
+    desc = pa.dense_desc(dtype, Hq, Hkv, 128, bs, case.num_blocks, case.k_pool.numel() * 2,
+                         case.v_pool.numel() * 2, part)
+    assert (pa.pa_decode_workspace_bytes(desc, case.num_seqs, max(ctx)) == 0) == single
+    run_case(case, part, check_write=False)
+
+
 def test_decode_is_deterministic_and_invariant_to_block_relabelling():
     ctx = [700, 33, 1600, 1]
     case = workloads.make_dense_case("tiny", seed=77, context_lens=ctx, num_blocks=200, num_q_heads=32,

@@ -253,19 +253,16 @@ def run_dense(name, steps, warmup, partition, flush):
     for _ in range(warmup):
         write()
         decode()
-    # The timed steps: flush, then write + decode between one pair of events (and decode alone
-    # between a second pair).
+    # The timed steps: flush, then write + decode between one pair of events (the decode alone is
+    # timed by call_stats below).
     ev_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         flush()
         ev_step[i][0].record(stream)
         write()
-        ev_dec[i][0].record(stream)
         decode()
-        ev_dec[i][1].record(stream)
         ev_step[i][1].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps

@@ -15,9 +15,10 @@
  * Conventions shared by every entry point:
  *   - Ownership: every pointer argument is caller-owned memory. "Device" means
  *     memory the GPU can read (hipMalloc / torch CUDA tensors); descriptors are
- *     host memory. The library allocates nothing, keeps no state between calls
- *     and may be called from several host threads. The one exception is
- *     pa_decode_no_alloc, whose scratch is a static device array of the library.
+ *     host memory. The library allocates nothing and may be called from several
+ *     host threads. Between calls it keeps, per device, only the CU count (read
+ *     once) and the address of pa_decode_no_alloc's scratch, a static device
+ *     array of the library.
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  *     stream). Work is enqueued asynchronously; no call synchronises or reads
  *     device memory on the host.

@@ -88,6 +88,17 @@ def test_decode_status_codes():
     assert decode(good_desc(partition_size=512), max_ctx=2048, ws=FAKE, ws_bytes=need - 1) == E.PA_ERR_WORKSPACE
 
 
+def test_decode_item_limit_counts_split_groups():
+    """Wave items (K/V heads x sequences x partitions) must stay below 2^31. Eight query heads per
+    K/V head at head_dim 64 or 256 take two waves per K/V head, so the same call is rejected there
+    while four query heads per K/V head pass this check (and then stop at the missing workspace)."""
+    def desc(hq):
+        return pa.dense_desc("f16", hq, 8, 64, 16, 64, 64 * 16 * 1024, 64 * 16 * 1024, 16)
+    S, max_ctx = 1 << 20, 2048          # 8 K/V heads x 2^20 sequences x 128 partitions = 2^30 items
+    assert decode(desc(32), num_seqs=S, max_ctx=max_ctx, bt_stride=128) == L.PA_ERR_WORKSPACE
+    assert decode(desc(64), num_seqs=S, max_ctx=max_ctx, bt_stride=128) == L.PA_ERR_UNSUPPORTED
+
+
 def test_automatic_partition_size():
     """partition_size 0: 1024 tokens if Hkv * S * ceil(max_ctx / 1024) >= 8192, else the largest of
     768, 512 with >= 2048 such items, else 256 (seen through the workspace size: S * Hq * parts *

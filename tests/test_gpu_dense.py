@@ -100,6 +100,9 @@ SHAPES = [
     ("f16", 64, 8, 64, 16, [2, 70, 1200], 128),
     ("bf16", 16, 4, 256, 16, [5, 300, 800], 0),
     ("f16", 16, 2, 256, 32, [9, 200, 1100], 256),
+    # block size 128, both kernels
+    ("bf16", 16, 4, 128, 128, [127, 128, 129, 900, 0], 0),
+    ("f16", 4, 4, 128, 128, [1, 255, 2000], 256),
 ]
 
 

@@ -97,6 +97,9 @@ SHAPES = [
     (16, 2, 64, 16, [2, 70, 1200], 128),
     (16, 4, 256, 16, [5, 300, 800], 0),
     (16, 2, 256, 32, [9, 200, 1100], 64),
+    # block size 128, matrix-core and vector kernels
+    (16, 4, 128, 128, [127, 128, 129, 900, 0], 0),
+    (4, 4, 128, 128, [1, 255, 2000], 256),
 ]
 
 

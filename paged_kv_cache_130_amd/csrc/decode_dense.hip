@@ -246,14 +246,20 @@ __global__ __launch_bounds__(256) void decode_dense_kernel(DenseDecodeParams p) 
             tile_step<BF16, D, G, true>(kk, vv, qr, m, l, acc, r, nvalid, p.scale_log2);
     };
 
-    // Two register slots: the loads of tile j+1 are in flight while tile j is computed.
-    uint4 k0[NL], v0[NL], k1[NL], v1[NL];
-    load(k0, v0, 0);
-    for (int j = 0; j < ntiles; j += 2) {
-        load(k1, v1, j + 1);
-        step(k0, v0, j);
-        load(k0, v0, j + 2);
-        if (j + 1 < ntiles) step(k1, v1, j + 1);
+    // A ring of kDepth tiles: the loads of the next kDepth - 1 tiles are in flight while one is
+    // computed (loads past the last tile read the cached dummy row). Single heads of 128 dims keep
+    // three tiles in flight at two waves per SIMD (177 registers): on the 13B-shaped decode that
+    // streams about 1% faster than one tile ahead at four waves per SIMD or two at three.
+    constexpr int kDepth = (D == 128 && G == 1) ? 4 : 2;
+    uint4 kb[kDepth][NL], vb[kDepth][NL];
+#pragma unroll
+    for (int i = 0; i < kDepth - 1; ++i) load(kb[i], vb[i], i);
+    for (int j = 0; j < ntiles; j += kDepth) {
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+            load(kb[(u + kDepth - 1) % kDepth], vb[(u + kDepth - 1) % kDepth], j + u + kDepth - 1);
+            if (u == 0 || j + u < ntiles) step(kb[u], vb[u], j + u);
+        }
     }
 
     // Merge the RPL row groups of the wave.

@@ -223,13 +223,18 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(DenseDecodeParams p) {
             f8_tile_step<D, G, true>(kk, vv, qr, m, l, acc, r, nvalid, p.scale_log2);
     };
 
-    uint4 k0[NL], v0[NL], k1[NL], v1[NL];
-    load(k0, v0, 0);
-    for (int j = 0; j < ntiles; j += 2) {
-        load(k1, v1, j + 1);
-        step(k0, v0, j);
-        load(k0, v0, j + 2);
-        if (j + 1 < ntiles) step(k1, v1, j + 1);
+    // A ring of kDepth tiles: the loads of the next kDepth - 1 tiles are in flight while one is
+    // computed (loads past the last tile read the cached dummy row).
+    constexpr int kDepth = 2;
+    uint4 kb[kDepth][NL], vb[kDepth][NL];
+#pragma unroll
+    for (int i = 0; i < kDepth - 1; ++i) load(kb[i], vb[i], i);
+    for (int j = 0; j < ntiles; j += kDepth) {
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+            load(kb[(u + kDepth - 1) % kDepth], vb[(u + kDepth - 1) % kDepth], j + u + kDepth - 1);
+            if (u == 0 || j + u < ntiles) step(kb[u], vb[u], j + u);
+        }
     }
 
     // Merge the RPL row groups of the wave (lanes that differ only in r), then apply V's scale.

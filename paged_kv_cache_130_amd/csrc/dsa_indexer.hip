@@ -319,7 +319,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(IndexerParams p) {
         int incl = wave_incl_scan((int)(c0 + c1), lane);
         if (lane == 63) s_wsum[wave][0] = incl;
         lds_sync();
-        for (int w = 0; w < wave; ++w) incl += s_wsum[w][0];
+        // All sixteen wave totals are read at once (a loop bounded by the wave index would wait for
+        // each read in turn, and every wave then waits for the last one at the next barrier).
+#pragma unroll
+        for (int w = 0; w < kTopkWaves; ++w) {
+            const int t = s_wsum[w][0];
+            incl += w < wave ? t : 0;
+        }
         const uint32_t before = (uint32_t)incl - c0 - c1;  // keys above digit 2047 - 2t
         if (before < (uint32_t)need && (uint32_t)need <= before + c0) {
             s_pick[0] = kBins - 1 - 2 * tid;

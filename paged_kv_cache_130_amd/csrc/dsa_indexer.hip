@@ -215,12 +215,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(IndexerParams p) {
 
     const int s = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = idx_ctx(p.context_lens[s], p);
     const int k = p.top_k;
     int32_t* pos_out = p.topk_pos + (int64_t)s * k;
     int32_t* slot_out = p.topk_slots + (int64_t)s * k;
     const int32_t* bt = p.block_tables + (int64_t)s * p.bt_stride;
     const float* src = p.scores + (int64_t)s * p.score_stride;
+    // The first kSelBlock scores and kTopkThreads block ids are read together with the context length
+    // rather than after it (from inside the score and table rows; what lies past the context is
+    // dropped), so that they arrive in the same round trip to memory.
+    float v0[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = j * kTopkThreads + tid;
+        v0[j] = i < p.score_stride ? src[i] : 0.f;
+    }
+    const int32_t bt0 = tid < p.bt_stride ? bt[tid] : 0;
+    const int n = idx_ctx(p.context_lens[s], p);
     const int nblk = (n + p.block_size - 1) >> p.block_size_log2;
     const bool bt_cached = nblk <= kBtCache;
 
@@ -254,7 +264,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(IndexerParams p) {
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
                 const int i = base + j * kTopkThreads + tid;
-                v[j] = i < n ? src[i] : 0.f;
+                v[j] = base == 0 ? v0[j] : i < n ? src[i] : 0.f;
             }
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
@@ -264,7 +274,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(IndexerParams p) {
         }
     }
     if (bt_cached)
-        for (int j = tid; j < nblk; j += kTopkThreads) s_bt[j] = bt[j];
+        for (int j = tid; j < nblk; j += kTopkThreads) s_bt[j] = j < kTopkThreads ? bt0 : bt[j];
     for (int i = tid; i < kBins; i += kTopkThreads) s_hist[0][i] = 0u;
     __syncthreads();
 
